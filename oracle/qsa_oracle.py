@@ -1,0 +1,287 @@
+"""Plain, slow reference for the QSA c4 hot path (TEST INFRASTRUCTURE ONLY).
+
+Only the tests, the smoke check and the CPU-baseline leg of the benchmark may
+import this module. The library path never does: it shares no code, constants,
+tables or helpers with the HIP kernels, and it reads no value they produce.
+
+Everything is computed from the bf16 input bits in float64, except the one step
+whose precision the pages fix (the block mean is taken in FP32).
+
+Sources, cited by title and section:
+  [QSA]  SGLang day-0 post on Qwen3.8-Flash-Next, section "Qwen Sparse Attention:
+         Retrieve Coarsely, Attend Precisely".
+  [IS]   same post, section "IndexShare MTP: Reusing the QSA Selection Across
+         Draft Steps"; and its "Model Architecture" list, IndexShare MTP item.
+
+Readings where the pages are silent or garbled (each is listed in the design doc):
+  R1  The scoring formula is cut off in [QSA]; the score of block c for a query is
+      s_c = sum_h w_h * max(0, q_h . k_c) over the 4 indexer heads, no 1/sqrt(d).
+  R2  "normalized" is the L2 norm, floored at 1e-12 (an all-zero mean stays zero).
+  R3  The block's rotary phase is 1-D RoPE at the block's first position 4c, with
+      rotate-half pairing (i, i+64) over all 128 dims and theta = 1e7; the angle of
+      pair i is 4c * theta**(-2i/128).  Normalise first, then rotate.
+  R4  The FP32 mean sums the four raw keys in token order, then scales by 1/4.
+  R5  Only complete blocks are scored: n_c(p) = (p+1) // 4 for a query at p; a block
+      the query's own token completes is visible.  The 0..3 tokens of the unfinished
+      block, 4*n_c .. p, are appended directly.
+  R6  Top-512 ties: higher score first, then lower block index.  All blocks are
+      kept when n_c <= 512.  The kept blocks are reported in ascending order.
+  R7  Sparse GQA: query head h reads KV head h // (16/2); logits are scaled by
+      1/sqrt(256); no sink, soft-cap or output gate; lse is the natural log.
+  R8  IndexShare: reuse step j attends to the captured positions plus p_cap+1 ..
+      p_cap+j (the positions drafted since the capture).
+  parity unpinned: fidelity to the real model's readings R1, R3 (pairing, rotary
+  fraction, theta) and R2's epsilon cannot be checked against the pages.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+TOPK_BLOCKS = 512
+BLOCK = 4                      # compression ratio c4
+MAX_SELECTED = TOPK_BLOCKS * BLOCK + BLOCK - 1   # 2051
+NORM_FLOOR = 1e-12
+
+
+# ---------------------------------------------------------------- number formats
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns -> float64 (exact)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def round_to_bf16(x) -> np.ndarray:
+    """float64 -> nearest bf16 value (ties to even), returned as float64.
+
+    bf16 keeps 8 significant bits and float32's exponent range, so the spacing of
+    the grid around x is 2**(e-8) where x = m * 2**e, 0.5 <= |m| < 1, and 2**-133
+    below the smallest normal.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    q = np.maximum(e, -125) - 8
+    y = np.ldexp(np.rint(np.ldexp(x, -q)), q)
+    big = np.abs(y) > 3.3895313892515355e38
+    return np.where(big, np.copysign(np.inf, x), y)
+
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    y = round_to_bf16(x).astype(np.float32)     # exact: y is on the bf16 grid
+    return (y.view(np.uint32) >> 16).astype(np.uint16)
+
+
+# ---------------------------------------------------------------- paged addressing
+
+def token_slot(page_row, t, page_size: int):
+    """Slot of logical token t in the raw K/V pool [QSA]: the raw K/V stays in the
+    ordinary paged pool, one token per slot."""
+    t = np.asarray(t, dtype=np.int64)
+    return np.asarray(page_row, dtype=np.int64)[t // page_size] * page_size + t % page_size
+
+
+def comp_slot(page_row, c, page_size: int):
+    """Slot of compressed block c in the compressed cache: the full slot of the
+    block's first token divided by 4, which is page aligned [QSA]."""
+    c = np.asarray(c, dtype=np.int64)
+    return token_slot(page_row, BLOCK * c, page_size) // BLOCK
+
+
+# ---------------------------------------------------------------- stage 1: keys
+
+def rotate(x, pos, theta: float) -> np.ndarray:
+    """Rotary phase of position `pos` on the last axis of x (reading R3)."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    inv_freq = theta ** (-(2.0 * np.arange(half)) / d)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv_freq
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[..., :half], x[..., half:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def block_mean_fp32(raw4_bits) -> np.ndarray:
+    """Mean of the 4 raw keys of a block, taken in FP32 [QSA] (reading R4).
+
+    raw4_bits: [..., 4, d] bf16 bits -> [..., d] float32.
+    """
+    k = bf16_to_f64(raw4_bits).astype(np.float32)
+    s = k[..., 0, :] + k[..., 1, :]
+    s = s + k[..., 2, :]
+    s = s + k[..., 3, :]
+    return s * np.float32(0.25)
+
+
+def compress_blocks(raw_bits, first_pos, theta: float) -> np.ndarray:
+    """Compressed index keys [QSA]: the FP32 mean of each block's 4 raw keys is
+    L2-normalised (R2), turned by the rotary phase of the block's first position
+    (R3) and stored as bf16.
+
+    raw_bits: [n, 4, d] bf16 bits; first_pos: [n] -> [n, d] bf16 bits.
+    """
+    m = block_mean_fp32(raw_bits).astype(np.float64)
+    norm = np.sqrt(np.sum(m * m, axis=-1, keepdims=True))
+    kbar = m / np.maximum(norm, NORM_FLOOR)
+    return f64_to_bf16_bits(rotate(kbar, first_pos, theta))
+
+
+def build_index_state(raw_bits, length: int, theta: float):
+    """Index state of a request after tokens 0..length-1 are ingested [QSA]:
+    one compressed key per complete block, and the raw keys of the unfinished
+    block's tokens in ring slots t % 4.
+
+    Returns (comp [length//4, d] bf16 bits, ring dict {slot: bits [d]}).
+    """
+    raw = np.asarray(raw_bits)[:length]
+    n_c = length // BLOCK
+    comp = compress_blocks(raw[:BLOCK * n_c].reshape(n_c, BLOCK, -1),
+                           BLOCK * np.arange(n_c), theta)
+    ring = {t % BLOCK: raw[t].copy() for t in range(BLOCK * n_c, length)}
+    return comp, ring
+
+
+# ---------------------------------------------------------------- stage 2: indexer
+
+def visible_blocks(p: int) -> int:
+    """Complete blocks visible to a query at position p (reading R5)."""
+    return (p + 1) // BLOCK
+
+
+def score_blocks(idx_q_bits, idx_w, comp_bits) -> np.ndarray:
+    """s_c = sum_h w_h * max(0, q_h . k_c) (reading R1) for every row k_c of comp.
+
+    idx_q_bits: [4, d]; idx_w: [4]; comp_bits: [n, d] -> [n] float64.
+    """
+    qh = bf16_to_f64(idx_q_bits)
+    k = bf16_to_f64(comp_bits)
+    w = np.asarray(idx_w, dtype=np.float64)
+    dots = k @ qh.T                               # [n, 4]
+    return np.maximum(dots, 0.0) @ w
+
+
+def select_blocks(scores, topk: int = TOPK_BLOCKS) -> np.ndarray:
+    """The best `topk` blocks [QSA], ties by lower index (R6), in ascending order."""
+    s = np.asarray(scores, dtype=np.float64)
+    n = s.shape[0]
+    if n <= topk:
+        return np.arange(n, dtype=np.int64)
+    order = np.lexsort((np.arange(n), -s))        # primary: -s, secondary: index
+    return np.sort(order[:topk]).astype(np.int64)
+
+
+def expand_positions(sel_blocks, p: int) -> np.ndarray:
+    """Logical token positions attended by a query at p [QSA]: the 4 tokens of
+    every kept block, then the 0..3 tokens of the unfinished block (R5)."""
+    sel = np.asarray(sel_blocks, dtype=np.int64)
+    full = (BLOCK * sel[:, None] + np.arange(BLOCK)[None, :]).reshape(-1)
+    pending = np.arange(BLOCK * visible_blocks(p), p + 1, dtype=np.int64)
+    return np.concatenate([full, pending])
+
+
+# ---------------------------------------------------------------- stage 3: sparse GQA
+
+def sparse_gqa(q_bits, k_rows_bits, v_rows_bits, sm_scale: float):
+    """Softmax attention of every query head over the given K/V rows [QSA]: the
+    values come from the raw, uncompressed cache (R7).
+
+    q_bits: [Hq, D]; k_rows_bits, v_rows_bits: [n, Hkv, D] -> (out [Hq, D], lse [Hq]).
+    """
+    q = bf16_to_f64(q_bits)
+    k = bf16_to_f64(k_rows_bits)
+    v = bf16_to_f64(v_rows_bits)
+    hq, hkv = q.shape[0], k.shape[1]
+    group = hq // hkv
+    out = np.zeros_like(q)
+    lse = np.zeros(hq)
+    for h in range(hq):
+        g = h // group
+        logits = (k[:, g, :] @ q[h]) * sm_scale
+        m = logits.max()
+        e = np.exp(logits - m)
+        out[h] = (e @ v[:, g, :]) / e.sum()
+        lse[h] = m + np.log(e.sum())
+    return out, lse
+
+
+# ---------------------------------------------------------------- whole queries
+
+def gather_rows(pool, page_row, positions, page_size: int):
+    return np.asarray(pool)[token_slot(page_row, positions, page_size)]
+
+
+def query(comp_bits, idx_q_bits, idx_w, q_bits, p: int, page_row, k_pool, v_pool,
+          page_size: int, sm_scale: float, topk: int = TOPK_BLOCKS):
+    """One query at position p through indexer and sparse GQA.
+
+    comp_bits: the request's compressed keys in logical block order (at least
+    visible_blocks(p) rows).  Returns a dict with scores, sel_blocks, positions,
+    out and lse.
+    """
+    n_c = visible_blocks(p)
+    scores = score_blocks(idx_q_bits, idx_w, comp_bits[:n_c])
+    sel = select_blocks(scores, topk)
+    pos = expand_positions(sel, p)
+    out, lse = sparse_gqa(q_bits, gather_rows(k_pool, page_row, pos, page_size),
+                          gather_rows(v_pool, page_row, pos, page_size), sm_scale)
+    return {"scores": scores, "sel_blocks": sel, "positions": pos, "out": out, "lse": lse}
+
+
+def indexshare_step(captured_positions, p_cap: int, j: int, q_bits, page_row, k_pool,
+                    v_pool, page_size: int, sm_scale: float):
+    """Reuse step j of the draft loop [IS] (reading R8): the captured selection
+    plus the positions drafted since, without running the indexer."""
+    pos = np.concatenate([np.asarray(captured_positions, dtype=np.int64),
+                          np.arange(p_cap + 1, p_cap + j + 1, dtype=np.int64)])
+    out, lse = sparse_gqa(q_bits, gather_rows(k_pool, page_row, pos, page_size),
+                          gather_rows(v_pool, page_row, pos, page_size), sm_scale)
+    return {"positions": pos, "out": out, "lse": lse}
+
+
+# ---------------------------------------------------------------- workload drivers
+# These take any object with the fields of a synthetic workload (lengths,
+# page_table, page_size, raw_idx_k, idx_q, idx_w, q, q_req, q_pos, k_pool, v_pool,
+# rope_theta, prefix_len, reuse_q, reuse_steps).
+
+def index_state(wl, b: int, length: int):
+    return build_index_state(wl.raw_idx_k[b], length, wl.rope_theta)
+
+
+def comp_cache_entries(wl, b: int, comp_bits):
+    """(slots, keys) of a request's compressed keys in the compressed cache layout."""
+    c = np.arange(comp_bits.shape[0])
+    return comp_slot(wl.page_table[b], c, wl.page_size), comp_bits
+
+
+def run_queries(wl, rows=None, sm_scale: float = 1.0 / 16.0, topk: int = TOPK_BLOCKS):
+    """Every (or the listed) query row of a decode / prefill / capture workload.
+
+    The compressed keys a query sees are those of the request's complete blocks
+    up to and including its own position; a block's key depends only on its own
+    four tokens, so one build over the request's tokens serves every row.
+    """
+    rows = range(wl.total_q) if rows is None else rows
+    comp_of = {}
+    res = {}
+    for t in rows:
+        b = int(wl.q_req[t])
+        p = int(wl.q_pos[t])
+        if b not in comp_of:
+            comp_of[b], _ = index_state(wl, b, int(wl.lengths[b]))
+        res[t] = query(comp_of[b], wl.idx_q[t], wl.idx_w[t], wl.q[t], p, wl.page_table[b],
+                       wl.k_pool, wl.v_pool, wl.page_size, sm_scale, topk)
+    return res
+
+
+def run_indexshare(wl, captured, sm_scale: float = 1.0 / 16.0):
+    """Reuse steps 1..reuse_steps for every request, from the capture results
+    `captured` (as returned by run_queries)."""
+    res = {}
+    for b in range(wl.batch):
+        p_cap = int(wl.q_pos[b])
+        for j in range(1, wl.reuse_steps + 1):
+            res[(j, b)] = indexshare_step(captured[b]["positions"], p_cap, j,
+                                          wl.reuse_q[j - 1, b], wl.page_table[b], wl.k_pool,
+                                          wl.v_pool, wl.page_size, sm_scale)
+    return res
