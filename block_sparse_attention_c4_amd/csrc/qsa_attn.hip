@@ -1,0 +1,324 @@
+// Stage 3: sparse GQA over the selected positions, read from the raw paged K/V.
+//
+// [SGLang day-0 post on Qwen3.8-Flash-Next, section "Qwen Sparse Attention:
+// Retrieve Coarsely, Attend Precisely"]: the softmax and the value aggregation
+// use the original, uncompressed K/V at the selected logical positions.
+// [Same post, section "IndexShare MTP: Reusing the QSA Selection Across Draft
+// Steps"]: a draft step attends to the captured selection plus the positions
+// drafted since, passed here as extra positions.
+//
+// Work: one work group (4 waves) per (query, KV head, split of the position
+// list).  A wave takes 32 positions per step, gathering K and V rows straight
+// through the page table (a block's 4 positions are 4 adjacent slots).  Both
+// products run on MFMA v_mfma_f32_16x16x32_bf16 with the 8 query heads of the
+// KV group in the 16-wide N dimension:
+//    S^T[pos, head] = K[pos, :] . Q^T[:, head]       (A = K rows, B = Q^T)
+//    O^T[dim, head] += V^T[dim, pos] . P^T[pos, head] (A = V^T, B = P^T)
+// The S^T accumulator layout (lane = head column, 4 positions per lane) is
+// exactly the B operand layout of the second product, so P never leaves the
+// lane.  V^T fragments come from each lane loading 16 B (8 dims) of its 8
+// positions and transposing the 8x8 bf16 tile in registers (v_perm_b32).
+// Softmax is online (running max and sum per head, log2 domain).  The 4 waves
+// merge through LDS; with several splits, a combine kernel merges the split
+// partials.
+#include "qsa_device.h"
+#include "qsa_launch.h"
+
+namespace qsa {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kChunk = 32;                      // positions per wave step
+constexpr int kPartFloats = 2 * kGroup + kGroup * kHeadDim;   // m[8], l[8], acc[8][256]
+constexpr int kAccPad = kHeadDim + 4;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__global__ void __launch_bounds__(kThreads)
+attn_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ q_req,
+            const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
+            const int32_t* __restrict__ page_table, int pt_stride, int page_size,
+            const int32_t* __restrict__ sel_pos, const int32_t* __restrict__ sel_count,
+            int sel_stride, const int32_t* __restrict__ extra_pos, int n_extra, float scale_log2,
+            int splits, int split_len, float* __restrict__ part, uint16_t* __restrict__ out,
+            float* __restrict__ lse) {
+  __shared__ float s_m[kWaves][kGroup];
+  __shared__ float s_l[kWaves][kGroup];
+  __shared__ float s_acc[kWaves][kGroup][kAccPad];
+
+  const int bid = blockIdx.x;
+  const int sp = bid % splits;
+  const int tg = bid / splits;
+  const int g = tg % kKVHeads;
+  const int t = tg / kKVHeads;
+  const int req = q_req ? q_req[t] : t;
+  const int cnt = sel_count[t];
+  const int total = cnt + n_extra;
+  const int start = sp * split_len;
+  const int end = min(start + split_len, total);
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int r = lane & 15;
+  const int j = lane >> 4;
+
+  const int32_t* pt_row = page_table + (size_t)req * pt_stride;
+  const int32_t* lst = sel_pos + (size_t)t * sel_stride;
+  const int32_t* ext = extra_pos ? extra_pos + (size_t)t * n_extra : nullptr;
+
+  // Q^T operand: head r of the group (zero for the 8 padding columns)
+  u32x4_t qf[8];
+  {
+    const uint16_t* qrow = q + ((size_t)t * kQHeads + g * kGroup + (r & 7)) * kHeadDim + 8 * j;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      qf[k] = (r < kGroup) ? ld16(qrow + 32 * k) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4_t acc[2][8];
+#pragma unroll
+  for (int gm = 0; gm < 2; ++gm)
+#pragma unroll
+    for (int tau = 0; tau < 8; ++tau) acc[gm][tau] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int cb = start + w * kChunk; cb < end; cb += kWaves * kChunk) {
+    // list index -> logical position (-1 = no position)
+    auto pos_at = [&](int i) -> int {
+      if (i >= end) return -1;
+      return i < cnt ? lst[i] : ext[i - cnt];
+    };
+    auto slot_of = [&](int p) -> int64_t { return p >= 0 ? token_slot(pt_row, p, page_size) : 0; };
+
+    // K rows of the two 16-position tiles: rows r and 16 + r
+    const int64_t sk0 = slot_of(pos_at(cb + r));
+    const int64_t sk1 = slot_of(pos_at(cb + 16 + r));
+    // V rows (and the logits this lane holds): positions 4j..4j+3 of each tile
+    int64_t sv[8];
+    bool ok[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int li = cb + (e < 4 ? 0 : 16) + 4 * j + (e & 3);
+      const int p = pos_at(li);
+      ok[e] = p >= 0;
+      sv[e] = slot_of(p);
+    }
+
+    u32x4_t kf0[8], kf1[8];
+    const uint16_t* k0 = k_pool + ((size_t)sk0 * kKVHeads + g) * kHeadDim + 8 * j;
+    const uint16_t* k1 = k_pool + ((size_t)sk1 * kKVHeads + g) * kHeadDim + 8 * j;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      kf0[k] = ld16(k0 + 32 * k);
+      kf1[k] = ld16(k1 + 32 * k);
+    }
+    u32x4_t vr[2][8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint16_t* vp = v_pool + ((size_t)sv[e] * kKVHeads + g) * kHeadDim + 8 * r;
+      vr[0][e] = ld16(vp);
+      vr[1][e] = ld16(vp + 128);
+      if (!ok[e]) {
+        vr[0][e] = u32x4_t{0u, 0u, 0u, 0u};
+        vr[1][e] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      s0 = mfma16(kf0[k], qf[k], s0);
+      s1 = mfma16(kf1[k], qf[k], s1);
+    }
+
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = ok[i] ? s0[i] * scale_log2 : -INFINITY;
+      x[4 + i] = ok[4 + i] ? s1[i] * scale_log2 : -INFINITY;
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    float pr[8];
+    float alpha = 1.f;
+    if (m_new == -INFINITY) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pr[e] = 0.f;
+    } else {
+      alpha = exp2f(m_run - m_new);   // m_run = -inf gives 0
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pr[e] = exp2f(x[e] - m_new);
+    }
+    float rs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rs += pr[e];
+    rs += shfl_xor_f(rs, 16);
+    rs += shfl_xor_f(rs, 32);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+
+    const u32x4_t pf = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                        pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
+#pragma unroll
+    for (int gm = 0; gm < 2; ++gm) {
+#pragma unroll
+      for (int tau = 0; tau < 8; ++tau) {
+        const uint32_t sel = (tau & 1) ? 0x07060302u : 0x05040100u;
+        const int dw = tau >> 1;
+        u32x4_t a;
+        a.x = __builtin_amdgcn_perm(vr[gm][1][dw], vr[gm][0][dw], sel);
+        a.y = __builtin_amdgcn_perm(vr[gm][3][dw], vr[gm][2][dw], sel);
+        a.z = __builtin_amdgcn_perm(vr[gm][5][dw], vr[gm][4][dw], sel);
+        a.w = __builtin_amdgcn_perm(vr[gm][7][dw], vr[gm][6][dw], sel);
+        f32x4_t c = acc[gm][tau] * alpha;
+        acc[gm][tau] = mfma16(a, pf, c);
+      }
+    }
+  }
+
+  // merge the 4 waves.  Lane (r, j) holds head r, dims 128*gm + 32*j + 8*i + tau.
+  if (r < kGroup) {
+    if (j == 0) {
+      s_m[w][r] = m_run;
+      s_l[w][r] = l_run;
+    }
+#pragma unroll
+    for (int gm = 0; gm < 2; ++gm)
+#pragma unroll
+      for (int tau = 0; tau < 8; ++tau)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_acc[w][r][128 * gm + 32 * j + 8 * i + tau] = acc[gm][tau][i];
+  }
+  __syncthreads();
+
+  const int h = tid >> 5;              // 0..7
+  const int d0 = (tid & 31) * 8;       // 8 dims per thread
+  float M = -INFINITY;
+#pragma unroll
+  for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, s_m[ww][h]);
+  float L = 0.f;
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float mw = s_m[ww][h];
+      if (mw == -INFINITY) continue;
+      const float sc = exp2f(mw - M);
+      L += sc * s_l[ww][h];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] += sc * s_acc[ww][h][d0 + e];
+    }
+  }
+
+  if (splits == 1) {
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    uint16_t* orow = out + ((size_t)t * kQHeads + g * kGroup + h) * kHeadDim + d0;
+    u32x4_t ov = {pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
+                  pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv)};
+    *reinterpret_cast<u32x4_t*>(orow) = ov;
+    if (lse && (tid & 31) == 0)
+      lse[(size_t)t * kQHeads + g * kGroup + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  } else {
+    float* pp = part + ((size_t)tg * splits + sp) * kPartFloats;
+    if ((tid & 31) == 0) {
+      pp[h] = M;
+      pp[kGroup + h] = L;
+    }
+    float* pa = pp + 2 * kGroup + h * kHeadDim + d0;
+    *reinterpret_cast<f32x4_t*>(pa) = f32x4_t{o[0], o[1], o[2], o[3]};
+    *reinterpret_cast<f32x4_t*>(pa + 4) = f32x4_t{o[4], o[5], o[6], o[7]};
+  }
+}
+
+// Merge the split partials of one (query, KV head): 256 threads, thread = (head, 8 dims).
+__global__ void __launch_bounds__(256)
+combine_kernel(const float* __restrict__ part, int splits, uint16_t* __restrict__ out,
+               float* __restrict__ lse) {
+  const int tg = blockIdx.x;
+  const int g = tg % kKVHeads;
+  const int t = tg / kKVHeads;
+  const int tid = threadIdx.x;
+  const int h = tid >> 5;
+  const int d0 = (tid & 31) * 8;
+  const float* base = part + (size_t)tg * splits * kPartFloats;
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) {
+    const float* pp = base + (size_t)s * kPartFloats;
+    if (pp[kGroup + h] > 0.f) M = fmaxf(M, pp[h]);
+  }
+  float L = 0.f;
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (M != -INFINITY) {
+    for (int s = 0; s < splits; ++s) {
+      const float* pp = base + (size_t)s * kPartFloats;
+      const float ls = pp[kGroup + h];
+      if (!(ls > 0.f)) continue;
+      const float sc = exp2f(pp[h] - M);
+      L += sc * ls;
+      const float* pa = pp + 2 * kGroup + h * kHeadDim + d0;
+      const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(pa);
+      const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(pa + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] += sc * a0[e];
+        o[4 + e] += sc * a1[e];
+      }
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint16_t* orow = out + ((size_t)t * kQHeads + g * kGroup + h) * kHeadDim + d0;
+  u32x4_t ov = {pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
+                pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv)};
+  *reinterpret_cast<u32x4_t*>(orow) = ov;
+  if (lse && (tid & 31) == 0)
+    lse[(size_t)t * kQHeads + g * kGroup + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
+}  // namespace
+
+void attn_plan(int total_q, int n_extra, int* splits, int* split_len) {
+  const int bound = kMaxSel + n_extra;
+  const int step = kWaves * kChunk;                    // 128 positions
+  const int pairs = total_q * kKVHeads;
+  int s = (1024 + pairs - 1) / pairs;
+  s = std::max(1, std::min(s, (bound + step - 1) / step));
+  int len = (bound + s - 1) / s;
+  len = ((len + step - 1) / step) * step;
+  *split_len = len;
+  *splits = (bound + len - 1) / len;
+}
+
+size_t attn_workspace_bytes(int total_q, int n_extra) {
+  int splits, len;
+  attn_plan(total_q, n_extra, &splits, &len);
+  if (splits == 1) return 0;
+  return (size_t)total_q * kKVHeads * splits * kPartFloats * sizeof(float);
+}
+
+hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
+  const float scale_log2 = a.sm_scale * kLog2e;
+  const int nblk = a.total_q * kKVHeads * a.splits;
+  hipLaunchKernelGGL(attn_kernel, dim3(nblk), dim3(kThreads), 0, stream, a.q, a.q_req, a.k_pool,
+                     a.v_pool, a.page_table, a.pt_stride, a.page_size, a.sel_pos, a.sel_count,
+                     a.sel_stride, a.extra_pos, a.n_extra, scale_log2, a.splits, a.split_len,
+                     a.part, a.out, a.lse);
+  if (a.splits > 1) {
+    hipLaunchKernelGGL(combine_kernel, dim3(a.total_q * kKVHeads), dim3(256), 0, stream, a.part,
+                       a.splits, a.out, a.lse);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qsa

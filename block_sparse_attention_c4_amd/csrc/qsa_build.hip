@@ -1,0 +1,123 @@
+// Stage 1: compressed index-key builder.
+//
+// [SGLang day-0 post on Qwen3.8-Flash-Next, section "Qwen Sparse Attention:
+// Retrieve Coarsely, Attend Precisely"]: the 4 raw indexer keys of a block are
+// averaged in FP32, normalised and turned by the rotary phase of the block's first
+// token; the result is one bf16 key stored at the block's first slot / 4.  The raw
+// keys of the unfinished block wait in a 4-slot ring per request.
+//
+// One wave per work group handles 4 blocks, 16 lanes per block.  Lane j (0..15)
+// of a block owns rotary pairs i = 4j .. 4j+3, i.e. dims 4j..4j+3 and
+// 64+4j..64+4j+3, so every rotation is lane local.  The mean is taken in FP32 in
+// token order (as the pages fix); the norm, the rotation and the rounding are
+// done in FP64, which keeps the phase exact to well below a bf16 step even at
+// position 262140 (an FP32 angle would be off by up to ~0.016 rad there).
+#include "qsa_device.h"
+#include "qsa_launch.h"
+
+namespace qsa {
+
+namespace {
+
+constexpr int kUnits = 4;   // blocks per work group
+
+__global__ void __launch_bounds__(64)
+build_kernel(const uint16_t* __restrict__ new_k, const int32_t* __restrict__ cu_new,
+             const int32_t* __restrict__ len_before, const int32_t* __restrict__ page_table,
+             int pt_stride, int page_size, uint16_t* __restrict__ ring,
+             uint16_t* __restrict__ comp, double theta) {
+  const int b = blockIdx.y;
+  const int off = cu_new[b];
+  const int n = cu_new[b + 1] - off;
+  if (n <= 0) return;
+  const int lb = len_before[b];
+  const int le = lb + n;
+  const int c0 = lb / kBlock;
+  const int unit = threadIdx.x >> 4;
+  const int j = threadIdx.x & 15;
+  const int c = c0 + blockIdx.x * kUnits + unit;
+  const bool complete = (kBlock * c + kBlock - 1) < le;
+
+  // read phase: FP32 sum in token order, then * 1/4
+  float m[8];
+  if (complete) {
+#pragma unroll
+    for (int tok = 0; tok < kBlock; ++tok) {
+      const int t = kBlock * c + tok;
+      const uint16_t* src = (t < lb) ? ring + ((size_t)b * kBlock + (t & 3)) * kIdxDim
+                                     : new_k + (size_t)(off + t - lb) * kIdxDim;
+      const u32x2_t a = *reinterpret_cast<const u32x2_t*>(src + 4 * j);
+      const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(src + 64 + 4 * j);
+      const float v[8] = {bf16lo(a.x), bf16hi(a.x), bf16lo(a.y), bf16hi(a.y),
+                          bf16lo(bb.x), bf16hi(bb.x), bf16lo(bb.y), bf16hi(bb.y)};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m[e] = (tok == 0) ? v[e] : (m[e] + v[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m[e] = m[e] * 0.25f;
+  }
+  // Every ring read of this launch happens above, in work group 0 (only block
+  // c0 can hold tokens older than this call).  Work group 0 writes the ring
+  // only after its reads.
+  __syncthreads();
+  if (blockIdx.x == 0 && (le % kBlock) != 0) {
+    const int first = max(kBlock * (le / kBlock), lb);
+    for (int t = first; t < le; ++t) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(new_k + (size_t)(off + t - lb) * kIdxDim);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(ring + ((size_t)b * kBlock + (t & 3)) * kIdxDim);
+      dst[threadIdx.x] = src[threadIdx.x];   // 64 lanes x 2 bf16 = 128 dims
+    }
+  }
+  if (!complete) return;
+
+  // L2 norm in FP64 over the 16 lanes of this block
+  double md[8];
+  double ss = 0.0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    md[e] = (double)m[e];
+    ss += md[e] * md[e];
+  }
+#pragma unroll
+  for (int sh = 1; sh < 16; sh <<= 1) ss += __shfl_xor(ss, sh, 64);
+  const double nrm = fmax(sqrt(ss), 1e-12);
+
+  const double pos = (double)(kBlock * c);
+  uint32_t outw[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = 4 * j + e;
+    const double inv_freq = pow(theta, -(2.0 * i) / (double)kIdxDim);
+    double s, co;
+    sincos(pos * inv_freq, &s, &co);
+    const double a = md[e] / nrm;
+    const double bv = md[4 + e] / nrm;
+    const double y0 = a * co - bv * s;
+    const double y1 = bv * co + a * s;
+    outw[e] = f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
+  }
+  // outw[e] packs (dim 4j+e, dim 64+4j+e); store dims 4j..4j+3 and 64+4j..+3
+  const int bpp = page_size / kBlock;   // compressed rows per page
+  const int64_t row = (int64_t)page_table[(size_t)b * pt_stride + c / bpp] * bpp + (c % bpp);
+  uint16_t* dst = comp + row * kIdxDim;
+  u32x2_t lo, hi;
+  lo.x = (outw[0] & 0xffffu) | (outw[1] << 16);
+  lo.y = (outw[2] & 0xffffu) | (outw[3] << 16);
+  hi.x = (outw[0] >> 16) | (outw[1] & 0xffff0000u);
+  hi.y = (outw[2] >> 16) | (outw[3] & 0xffff0000u);
+  *reinterpret_cast<u32x2_t*>(dst + 4 * j) = lo;
+  *reinterpret_cast<u32x2_t*>(dst + 64 + 4 * j) = hi;
+}
+
+}  // namespace
+
+hipError_t launch_build(const BuildArgs& a, hipStream_t stream) {
+  // blocks touched by n new tokens starting anywhere: at most n/4 + 2
+  const int units = a.max_new / kBlock + 2;
+  dim3 grid((units + kUnits - 1) / kUnits, a.batch);
+  hipLaunchKernelGGL(build_kernel, grid, dim3(64), 0, stream, a.new_k, a.cu_new, a.len_before,
+                     a.page_table, a.pt_stride, a.page_size, a.ring, a.comp, (double)a.theta);
+  return hipGetLastError();
+}
+
+}  // namespace qsa

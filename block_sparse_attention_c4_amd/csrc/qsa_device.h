@@ -1,0 +1,85 @@
+// Device-side helpers shared by the QSA c4 kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+constexpr int kBlock = 4;        // tokens per compressed block
+constexpr int kTopK = 512;       // blocks kept per query
+constexpr int kMaxSel = 2051;    // 4 * 512 + 3
+constexpr int kIdxHeads = 4;
+constexpr int kIdxDim = 128;
+constexpr int kQHeads = 16;
+constexpr int kKVHeads = 2;
+constexpr int kGroup = kQHeads / kKVHeads;   // 8 query heads per KV head
+constexpr int kHeadDim = 256;
+constexpr int kMaxContext = 262144;
+constexpr int kMaxBlocks = kMaxContext / kBlock;   // 65536
+constexpr int kScoreGroup = 16;  // blocks per group maximum written by the scorer
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// double -> bf16 bits, round to nearest even, without double rounding: the value
+// is first cut to float toward zero with a sticky last bit (round to odd), which
+// keeps 16 guard bits below bf16's last place.
+__device__ __forceinline__ uint32_t f64_to_bf16(double x) {
+  float f = __double2float_rz(x);
+  uint32_t u = __float_as_uint(f);
+  if ((double)f != x) u |= 1u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Order-preserving unsigned key of a float (larger float -> larger key).
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Cross-lane moves within a row of 16 lanes (DPP).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+// Sum over the 16 lanes of a row; every lane of the row receives the sum.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xb1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_f<0x4e>(v);    // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);   // row_half_mirror
+  v += dpp_f<0x140>(v);   // row_mirror
+  return v;
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ u32x4_t ld16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// Slot of logical token t of a request (row of its page table).
+__device__ __forceinline__ int64_t token_slot(const int32_t* pt_row, int t, int page_size) {
+  return (int64_t)pt_row[t / page_size] * page_size + (t % page_size);
+}
+
+}  // namespace qsa

@@ -1,0 +1,64 @@
+// Internal launch interface between the C ABI (qsa_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qsa {
+
+struct BuildArgs {
+  int batch, max_new, page_size, pt_stride;
+  float theta;
+  const uint16_t* new_k;
+  const int32_t* cu_new;
+  const int32_t* len_before;
+  const int32_t* page_table;
+  uint16_t* ring;
+  uint16_t* comp;
+};
+hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
+
+struct IndexArgs {
+  int total_q, max_pos, page_size, pt_stride, sel_stride;
+  const uint16_t* idx_q;
+  const float* idx_w;
+  const int32_t* q_req;
+  const int32_t* q_pos;
+  const int32_t* page_table;
+  const uint16_t* comp;
+  int32_t* sel_blocks;
+  int32_t* sel_pos;
+  int32_t* sel_count;
+  // workspace
+  float* scores;       // [total_q, score_stride]
+  float* gmax;         // [total_q, score_stride / 16]
+  int score_stride;    // multiple of 64, >= max_pos / 4
+};
+size_t index_workspace_bytes(int total_q, int max_pos);
+void index_workspace_carve(IndexArgs& a, void* ws);
+hipError_t launch_index(const IndexArgs& a, hipStream_t stream);
+
+struct AttnArgs {
+  int total_q, page_size, pt_stride, sel_stride, n_extra;
+  float sm_scale;
+  const uint16_t* q;
+  const int32_t* q_req;      // NULL: query t reads request t
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* page_table;
+  const int32_t* sel_pos;
+  const int32_t* sel_count;
+  const int32_t* extra_pos;  // may be NULL
+  uint16_t* out;
+  float* lse;                // may be NULL
+  // workspace (split partials)
+  float* part;               // [total_q, kv, splits, 8 + 8 + 8*256]
+  int splits;
+  int split_len;             // positions per split (multiple of 128)
+};
+void attn_plan(int total_q, int n_extra, int* splits, int* split_len);
+size_t attn_workspace_bytes(int total_q, int n_extra);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace qsa

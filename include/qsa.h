@@ -1,0 +1,199 @@
+/*
+ * qsa.h - C ABI of the QSA c4 hot path on MI355X (gfx950).
+ *
+ * QSA ("Qwen Sparse Attention", compression ratio 4) attends each query to at
+ * most 2051 positions of a long context.  A light indexer picks them: every 4
+ * tokens' raw indexer keys are compressed into one key, the query scores every
+ * visible compressed block, the best 512 blocks are kept and expanded back to
+ * token positions, and the 0..3 tokens of the unfinished block are appended.
+ * Attention then reads those positions from the raw, uncompressed paged K/V
+ * cache.  [SGLang day-0 post on Qwen3.8-Flash-Next, section "Qwen Sparse
+ * Attention: Retrieve Coarsely, Attend Precisely"; section "IndexShare MTP:
+ * Reusing the QSA Selection Across Draft Steps" for the reuse step.]
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless marked "host".  The caller owns every
+ *    buffer; the library never allocates, frees or synchronises, and reads no
+ *    device memory back to the host.  Scratch memory comes from the caller's
+ *    workspace, sized by qsa_workspace_bytes().
+ *  - bf16 tensors are passed as uint16_t bit patterns; all are row-major and
+ *    densely packed in the shapes given.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    is ordered after earlier work on it.  Calls are graph-capturable: no host
+ *    readback and no data-dependent launch shape.
+ *  - Host-side arguments are validated before anything is launched; on error a
+ *    status other than QSA_OK is returned and nothing is enqueued.  Contents of
+ *    device arrays (page tables, positions, counts) are trusted: they must lie
+ *    in the ranges stated below.
+ *  - Reentrant; no mutable global state.
+ *
+ * Supported shapes: num_q_heads = 16, num_kv_heads = 2, head_dim = 256,
+ * idx_heads = 4, idx_dim = 128, page_size a multiple of 16 (64 in practice),
+ * positions 0 .. QSA_MAX_CONTEXT-1.  Anything else returns QSA_E_UNSUPPORTED.
+ *
+ * Layouts:
+ *  - Raw K/V pool (the ordinary paged cache): k_pool, v_pool [slots, Hkv, D].
+ *    Token t of request b lives in slot
+ *        page_table[b * pt_stride + t / page_size] * page_size + t % page_size.
+ *  - Compressed key cache: comp_cache [slots / 4, idx_dim].  Block c (tokens
+ *    4c..4c+3) of request b lives at row  slot(4c) / 4  (the block's first
+ *    slot over 4, page aligned), so it follows the page's ownership.
+ *  - Ring: ring [batch, 4, idx_dim] holds the raw indexer keys of a request's
+ *    unfinished block; token t sits in slot t % 4.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSA_BLOCK 4            /* tokens per compressed block (c4)            */
+#define QSA_TOPK 512           /* blocks kept per query                       */
+#define QSA_MAX_SEL 2051       /* 4 * 512 + 3 positions at most per query     */
+#define QSA_MAX_CONTEXT 262144 /* positions 0 .. 262143                       */
+#define QSA_MAX_EXTRA 8        /* extra (drafted) positions per reuse query   */
+
+typedef struct qsa_dims {
+  int32_t num_q_heads;  /* attention query heads              (16)          */
+  int32_t num_kv_heads; /* attention K/V heads                (2)           */
+  int32_t head_dim;     /* attention head size                (256)         */
+  int32_t idx_heads;    /* indexer query heads                (4)           */
+  int32_t idx_dim;      /* indexer head size                  (128)         */
+  int32_t page_size;    /* tokens per page; multiple of 16    (64)          */
+  float rope_theta;     /* rotary base of the indexer keys    (1e7)         */
+  float sm_scale;       /* attention logit scale              (1/sqrt(256)) */
+} qsa_dims;
+
+enum qsa_status {
+  QSA_OK = 0,
+  QSA_E_NULL = 1,        /* a required pointer is NULL                       */
+  QSA_E_SHAPE = 2,       /* a size or stride is out of range                 */
+  QSA_E_UNSUPPORTED = 3, /* dims other than the compiled ones                */
+  QSA_E_WORKSPACE = 4,   /* workspace missing or smaller than required       */
+  QSA_E_HIP = 5          /* a HIP launch failed (see hipGetLastError)        */
+};
+
+enum qsa_op {
+  QSA_OP_INDEX_TOPK = 1,
+  QSA_OP_GQA_DECODE = 2,
+  QSA_OP_GQA_PREFILL = 3
+};
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* qsa_status_string(int status);
+
+/* Workspace bytes that `op` needs for `total_q` queries.
+ *   INDEX_TOPK:  max_pos = an upper bound on every q_pos + 1 (host).
+ *   GQA_DECODE / GQA_PREFILL: n_extra = columns of extra_pos (0 for prefill).
+ * Returns 0 for bad arguments.  The workspace must be 256-byte aligned. */
+size_t qsa_workspace_bytes(const qsa_dims* dims, int op, int32_t total_q, int32_t max_pos,
+                           int32_t n_extra);
+
+/* Stage 1 - compressed index-key builder.  [QSA section: every 4 raw index keys
+ * are averaged in FP32, normalised, turned with the first token's rotary
+ * position and kept as one BF16 compressed key; a 4-slot per-request ring holds
+ * the raw keys of the unfinished block; compressed keys sit at full_slot / 4.]
+ *
+ * Ingests the raw indexer keys of new tokens len_before[b] .. len_before[b] +
+ * n_b - 1 of every request b (n_b = cu_new[b+1] - cu_new[b]).  For each block
+ * that becomes complete, its key is
+ *     m   = ((k0 + k1) + k2) + k3, times 1/4, in FP32 (token order);
+ *     k   = m / max(||m||_2, 1e-12);
+ *     key = k with pair (i, i+64) turned by angle 4c * theta^(-2i/128);
+ * rounded to bf16 (nearest-even) and stored at comp_cache row slot(4c) / 4.
+ * Raw keys of earlier tokens of the block are read from the ring; raw keys of
+ * tokens left in an unfinished block are written to ring slots t % 4.
+ *
+ *   new_idx_k  [total_new, idx_dim] bf16  raw keys, request-major (read)
+ *   cu_new     [batch + 1] int32          offsets into new_idx_k (read)
+ *   len_before [batch] int32              tokens ingested before this call (read)
+ *   total_new, max_new (host)             cu_new[batch] and max n_b
+ *   page_table [batch, pt_stride] int32   physical page of each logical page;
+ *                                         must cover every written block
+ *   ring       [batch, 4, idx_dim] bf16   in/out
+ *   comp_cache [rows, idx_dim] bf16       out (rows of completed blocks only)
+ */
+int qsa_build_index_keys(const qsa_dims* dims, int32_t batch, const uint16_t* new_idx_k,
+                         const int32_t* cu_new, const int32_t* len_before, int32_t total_new,
+                         int32_t max_new, const int32_t* page_table, int32_t pt_stride,
+                         uint16_t* ring, uint16_t* comp_cache, void* stream);
+
+/* Stage 2 - indexer: score, top-512, expansion.  [QSA section: a query scores
+ * the visible compressed blocks, the best 512 are kept and expanded to 2048
+ * token positions, and the 0..3 tokens of the unfinished block are appended,
+ * at most 2051 positions.]
+ *
+ * For query t at position p = q_pos[t] of request b = q_req[t]:
+ *   n_c = (p + 1) / 4 complete blocks are visible;
+ *   s_c = sum_h w_h * max(0, q_h . key_c)  for c < n_c  (FP32 accumulation);
+ *   the 512 best blocks are kept (all if n_c <= 512), higher score first, ties
+ *   to the lower block index, and written ascending to sel_blocks (-1 pad);
+ *   sel_pos gets 4c..4c+3 of each kept block, ascending, then 4*n_c .. p;
+ *   sel_count = 4 * min(n_c, 512) + (p + 1) % 4; the rest of the row is -1.
+ *
+ *   idx_q      [total_q, idx_heads, idx_dim] bf16  indexer queries (rotary applied)
+ *   idx_w      [total_q, idx_heads] float          per-head weights w_h
+ *   q_req, q_pos [total_q] int32                   request and position of each query
+ *   max_pos (host)                                 > every q_pos; <= QSA_MAX_CONTEXT
+ *   comp_cache                                     as written by the builder
+ *   sel_blocks [total_q, 512] int32   out
+ *   sel_pos    [total_q, sel_stride] int32 out, sel_stride >= 2051
+ *   sel_count  [total_q] int32        out
+ *   workspace  >= qsa_workspace_bytes(QSA_OP_INDEX_TOPK, total_q, max_pos, 0)
+ */
+int qsa_index_topk(const qsa_dims* dims, int32_t batch, int32_t total_q, const uint16_t* idx_q,
+                   const float* idx_w, const int32_t* q_req, const int32_t* q_pos,
+                   int32_t max_pos, const int32_t* page_table, int32_t pt_stride,
+                   const uint16_t* comp_cache, int32_t* sel_blocks, int32_t* sel_pos,
+                   int32_t sel_stride, int32_t* sel_count, void* workspace, size_t ws_bytes,
+                   void* stream);
+
+/* Stage 3 - sparse GQA, decode (one query per request).  [QSA section: the
+ * final softmax and value aggregation use the original, uncompressed K/V; IndexShare
+ * section: a draft step reuses the captured selection plus the positions drafted
+ * since the capture.]
+ *
+ * For request b, head h (KV head g = h / (Hq / Hkv)) over the position list
+ * S = sel_pos[b, 0 .. sel_count[b]-1]  plus every extra_pos[b, j] >= 0:
+ *   out[b, h] = sum_t softmax_t(sm_scale * q[b, h] . K[t, g]) * V[t, g],
+ *   lse[b, h] = log(sum_t exp(sm_scale * q[b, h] . K[t, g]))   (natural log).
+ * Positions must be distinct and their pages mapped; an empty S gives out = 0
+ * and lse = -inf.
+ *
+ *   q          [batch, Hq, D] bf16
+ *   k_pool, v_pool [slots, Hkv, D] bf16
+ *   sel_pos [batch, sel_stride], sel_count [batch] int32 (sel_count <= sel_stride)
+ *   extra_pos  [batch, n_extra] int32 or NULL (n_extra = 0); n_extra <= QSA_MAX_EXTRA
+ *   out        [batch, Hq, D] bf16 out;  lse [batch, Hq] float out or NULL
+ *   workspace  >= qsa_workspace_bytes(QSA_OP_GQA_DECODE, batch, 0, n_extra)
+ */
+int qsa_sparse_gqa_decode(const qsa_dims* dims, int32_t batch, const uint16_t* q,
+                          const uint16_t* k_pool, const uint16_t* v_pool,
+                          const int32_t* page_table, int32_t pt_stride, const int32_t* sel_pos,
+                          const int32_t* sel_count, int32_t sel_stride, const int32_t* extra_pos,
+                          int32_t n_extra, uint16_t* out, float* lse, void* workspace,
+                          size_t ws_bytes, void* stream);
+
+/* Stage 3 - sparse GQA over a chunk of prefill queries: as the decode call, with
+ * query t reading request q_req[t] and no extra positions.  [QSA section: for
+ * prefill the expanded indices feed sparse GQA.]
+ *
+ *   q [total_q, Hq, D] bf16;  q_req [total_q] int32;  out [total_q, Hq, D] bf16;
+ *   lse [total_q, Hq] float or NULL;
+ *   workspace >= qsa_workspace_bytes(QSA_OP_GQA_PREFILL, total_q, 0, 0)
+ */
+int qsa_sparse_gqa_prefill(const qsa_dims* dims, int32_t total_q, const uint16_t* q,
+                           const int32_t* q_req, const uint16_t* k_pool, const uint16_t* v_pool,
+                           const int32_t* page_table, int32_t pt_stride, const int32_t* sel_pos,
+                           const int32_t* sel_count, int32_t sel_stride, uint16_t* out,
+                           float* lse, void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

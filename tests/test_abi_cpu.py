@@ -1,0 +1,127 @@
+"""Host-side checks of libqsa.so that need no GPU: it loads, exports every
+function include/qsa.h declares, and rejects bad arguments with the documented
+status before anything is launched."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_c4_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qsa.h")
+FAKE = 0x10000   # a non-NULL, 256-byte aligned address that is never dereferenced
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(qsa_\w+)\s*\(", text, re.M)))
+
+
+def test_header_functions_are_exported():
+    names = declared()
+    assert set(names) == set(B.EXPORTED), names
+    L = B.lib()
+    for n in names:
+        assert getattr(L, n) is not None
+
+
+def test_status_strings():
+    for st in range(6):
+        assert B.status_string(st).startswith("QSA_")
+    assert "unknown" in B.status_string(99)
+
+
+def test_workspace_sizes():
+    d = B.default_dims()
+    a = B.qsa_workspace_bytes(d, B.QSA_OP_INDEX_TOPK, 32, 131072)
+    b = B.qsa_workspace_bytes(d, B.QSA_OP_INDEX_TOPK, 32, 262144)
+    assert 0 < a < b and a % 256 == 0
+    assert B.qsa_workspace_bytes(d, B.QSA_OP_INDEX_TOPK, 32, 262145) == 0
+    assert B.qsa_workspace_bytes(d, B.QSA_OP_GQA_DECODE, 32, 0, 9) == 0
+    assert B.qsa_workspace_bytes(d, B.QSA_OP_GQA_DECODE, 32, 0, 4) > 0
+    assert B.qsa_workspace_bytes(d, 99, 32, 1) == 0
+    bad = B.default_dims()
+    bad.num_q_heads = 32
+    assert B.qsa_workspace_bytes(bad, B.QSA_OP_INDEX_TOPK, 32, 4096) == 0
+
+
+def _topk(dims=None, **kw):
+    d = dims or B.default_dims()
+    args = dict(batch=1, total_q=1, idx_q=FAKE, idx_w=FAKE, q_req=FAKE, q_pos=FAKE, max_pos=4096,
+                page_table=FAKE, pt_stride=64, comp=FAKE, sel_blocks=FAKE, sel_pos=FAKE, sel_stride=2052,
+                sel_count=FAKE, ws=FAKE, ws_bytes=1 << 30)
+    args.update(kw)
+    a = args
+    return B.lib().qsa_index_topk(ctypes.byref(d), a["batch"], a["total_q"], a["idx_q"], a["idx_w"],
+                                  a["q_req"], a["q_pos"], a["max_pos"], a["page_table"], a["pt_stride"],
+                                  a["comp"], a["sel_blocks"], a["sel_pos"], a["sel_stride"],
+                                  a["sel_count"], a["ws"], a["ws_bytes"], None)
+
+
+def test_index_topk_validation():
+    assert _topk(total_q=0) == B.QSA_OK                        # nothing to do, nothing launched
+    assert _topk(idx_q=None) == B.QSA_E_NULL
+    assert _topk(sel_count=None) == B.QSA_E_NULL
+    assert _topk(sel_stride=2050) == B.QSA_E_SHAPE
+    assert _topk(max_pos=262145) == B.QSA_E_SHAPE
+    assert _topk(max_pos=0) == B.QSA_E_SHAPE
+    assert _topk(idx_q=FAKE + 2) == B.QSA_E_SHAPE             # misaligned bf16 rows
+    assert _topk(ws=None) == B.QSA_E_WORKSPACE
+    assert _topk(ws_bytes=16) == B.QSA_E_WORKSPACE
+    assert _topk(ws=FAKE + 16) == B.QSA_E_WORKSPACE           # not 256-byte aligned
+    bad = B.default_dims()
+    bad.idx_dim = 64
+    assert _topk(dims=bad) == B.QSA_E_UNSUPPORTED
+    bad = B.default_dims()
+    bad.page_size = 24
+    assert _topk(dims=bad) == B.QSA_E_UNSUPPORTED
+    assert B.lib().qsa_index_topk(None, 1, 1, *([None] * 4), 10, None, 1, None, None, None, 2052,
+                                  None, None, 0, None) == B.QSA_E_NULL
+
+
+def test_build_validation():
+    d = B.default_dims()
+    L = B.lib()
+    call = lambda **k: L.qsa_build_index_keys(
+        ctypes.byref(k.get("d", d)), k.get("batch", 2), k.get("new", FAKE), FAKE, FAKE,
+        k.get("total", 8), k.get("maxn", 4), FAKE, k.get("pts", 16), FAKE, k.get("comp", FAKE), None)
+    assert call(total=0, maxn=0) == B.QSA_OK
+    assert call(new=None) == B.QSA_E_NULL
+    assert call(comp=None) == B.QSA_E_NULL
+    assert call(maxn=9) == B.QSA_E_SHAPE                      # max_new > total_new
+    assert call(pts=0) == B.QSA_E_SHAPE
+    assert call(batch=-1) == B.QSA_E_SHAPE
+    assert call(new=FAKE + 2) == B.QSA_E_SHAPE
+    bad = B.default_dims()
+    bad.num_kv_heads = 4
+    assert call(d=bad) == B.QSA_E_UNSUPPORTED
+
+
+def test_gqa_validation():
+    d = B.default_dims()
+    L = B.lib()
+    ws = B.qsa_workspace_bytes(d, B.QSA_OP_GQA_DECODE, 8, 0, 4)
+
+    def dec(**k):
+        return L.qsa_sparse_gqa_decode(ctypes.byref(d), k.get("batch", 8), k.get("q", FAKE), FAKE, FAKE,
+                                       FAKE, 64, FAKE, FAKE, 2052, k.get("extra", FAKE), k.get("n_extra", 4),
+                                       k.get("out", FAKE), None, k.get("ws", FAKE), k.get("ws_bytes", ws), None)
+    assert dec(batch=0) == B.QSA_OK
+    assert dec(q=None) == B.QSA_E_NULL
+    assert dec(out=None) == B.QSA_E_NULL
+    assert dec(extra=None) == B.QSA_E_NULL                     # n_extra > 0 needs the array
+    assert dec(n_extra=9) == B.QSA_E_SHAPE
+    assert dec(n_extra=-1) == B.QSA_E_SHAPE
+    assert dec(ws_bytes=ws - 1) == B.QSA_E_WORKSPACE
+    assert dec(q=FAKE + 8) == B.QSA_E_SHAPE
+    assert L.qsa_sparse_gqa_prefill(ctypes.byref(d), 4, FAKE, None, FAKE, FAKE, FAKE, 64, FAKE, FAKE,
+                                    2052, FAKE, None, None, 0, None) == B.QSA_E_NULL   # q_req missing
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", "/nonexistent/libqsa.so")
+    with pytest.raises(ImportError):
+        B.lib()

@@ -1,0 +1,316 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Stage-isolated checks feed each stage the oracle's output of the previous stage
+(so a legitimate 1-ulp key difference cannot cascade); end-to-end checks run the
+three GPU stages back to back.  Small ragged workloads are checked on every
+query; the full-size workloads on every request (decode) or a sample of query
+rows (prefill), in the same launch configuration the benchmark times.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_c4_amd import runner, synth
+from oracle import qsa_oracle as O
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need the MI355X"
+    return "cuda:0"
+
+
+def full(name):
+    if name not in _CACHE:
+        P.log(f"[gen] {name}")
+        _CACHE[name] = synth.FULL_SIZE[name]()
+    return _CACHE[name]
+
+
+SMALL = {
+    # lengths cover: empty selection, dense (n_c <= 512), n_c = 512 / 513, the direct
+    # top-k path (n_c < 8192) and the group-filtered path (n_c >= 8192)
+    "decode_ragged": lambda: synth.make_workload(
+        "decode_ragged", "decode", 301, [1, 2, 5, 600, 2048, 2051, 2052, 2055, 5003, 33001, 40000],
+        hot_per_req=8),
+    "decode_page16": lambda: synth.make_workload(
+        "decode_page16", "decode", 302, [37, 2060, 9000, 35000], hot_per_req=4, page_size=16),
+    "prefill_ragged": lambda: synth.make_workload(
+        "prefill_ragged", "prefill", 303, [2101, 33333], chunk=37),
+    "indexshare_small": lambda: synth.make_workload(
+        "indexshare_small", "indexshare", 304, [4100, 33003, 700], reuse_steps=3),
+}
+
+
+def small(name):
+    key = "small:" + name
+    if key not in _CACHE:
+        _CACHE[key] = SMALL[name]()
+    return _CACHE[key]
+
+
+def _device(wl):
+    P.log(f"[upload] {wl.name} B={wl.batch} T={wl.total_q} pages={wl.num_pages}")
+    return runner.DeviceWorkload(wl, _gpu())
+
+
+def _rows(wl, sample):
+    if sample is None or wl.total_q <= sample:
+        return list(range(wl.total_q))
+    rng = np.random.default_rng(7)
+    head = list(range(8)) + list(range(wl.total_q - 8, wl.total_q))
+    mid = rng.choice(np.arange(8, wl.total_q - 8), size=sample - 16, replace=False)
+    return sorted(set(head) | set(int(x) for x in mid))
+
+
+def _upload_oracle_comp(dw, wl, states):
+    comp = np.zeros(dw.comp.shape, dtype=np.uint16)
+    for b, (keys, _) in enumerate(states):
+        if keys.shape[0]:
+            comp[O.comp_slot(wl.page_table[b], np.arange(keys.shape[0]), wl.page_size)] = keys
+    dw.comp.copy_(torch.from_numpy(comp.view(np.int16)))
+
+
+# ------------------------------------------------------------------ stage 1
+
+def _check_builder(wl):
+    dw = _device(wl)
+    dw.build_prefix()
+    dw.build_step()
+    torch.cuda.synchronize()
+    states = P.oracle_index_states(wl)
+    n, nd = P.check_comp_cache(wl, dw.comp_numpy(), states)
+    P.check_ring(dw.ring_numpy(), states)
+    P.log(f"[builder] {wl.name}: {n} keys, {nd} not bit-identical (<= 1 ulp)")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_builder_small(name):
+    _check_builder(small(name))
+
+
+@pytest.mark.parametrize("name", list(synth.FULL_SIZE))
+def test_builder_full(name):
+    _check_builder(full(name))
+
+
+def test_builder_incremental_decode_matches_bulk():
+    # ingest token by token (decode steps) and compare with one bulk ingest
+    wl = synth.make_workload("inc", "decode", 305, [70, 23], page_order="shuffled")
+    dw = _device(wl)
+    dims = dw.dims
+    from block_sparse_attention_c4_amd import binding as B
+    for t in range(int(wl.lengths.max())):
+        live = [b for b in range(wl.batch) if t < wl.lengths[b]]
+        keys = np.stack([wl.raw_idx_k[b][t] for b in range(wl.batch) if t < wl.lengths[b]])
+        cu = np.zeros(wl.batch + 1, np.int32)
+        for b in range(wl.batch):
+            cu[b + 1] = cu[b] + (1 if b in live else 0)
+        B.qsa_build_index_keys(dims, wl.batch, runner._u16(keys, dw.dev), runner._i32(cu, dw.dev),
+                               runner._i32(np.full(wl.batch, t), dw.dev), len(live), 1,
+                               dw.page_table, dw.pt_stride, dw.ring, dw.comp)
+    torch.cuda.synchronize()
+    states = P.oracle_index_states(wl)
+    P.check_comp_cache(wl, dw.comp_numpy(), states)
+    P.check_ring(dw.ring_numpy(), states)
+
+
+# ------------------------------------------------------------------ stage 2 (fed oracle keys)
+
+def _check_index_stage(wl, sample=None):
+    dw = _device(wl)
+    states = P.oracle_index_states(wl)
+    _upload_oracle_comp(dw, wl, states)
+    dw.index()
+    torch.cuda.synchronize()
+    gb = dw.sel_blocks.cpu().numpy()
+    gp = dw.sel_pos.cpu().numpy()
+    gc = dw.sel_count.cpu().numpy()
+    rows = _rows(wl, sample)
+    res = O.run_queries(wl, rows)
+    ties = 0
+    for t in rows:
+        where = f"{wl.name} row {t} (p={int(wl.q_pos[t])})"
+        if P.check_selection(gb[t], res[t], where):
+            P.check_positions(gp[t], int(gc[t]), res[t], where)
+        else:
+            ties += 1
+            P.check_positions_valid(gp[t], int(gc[t]), gb[t], int(wl.q_pos[t]), where)
+    P.log(f"[index] {wl.name}: {len(rows)} rows, {ties} resolved by boundary ties")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_index_stage_small(name):
+    _check_index_stage(small(name))
+
+
+@pytest.mark.parametrize("name", list(synth.FULL_SIZE))
+def test_index_stage_full(name):
+    _check_index_stage(full(name), sample=48)
+
+
+def test_index_all_ties():
+    # zero indexer queries: every score is 0, so the lowest 512 blocks win
+    wl = synth.make_workload("ties", "decode", 306, [9000, 40000, 2100])
+    wl.idx_q[:] = 0
+    _check_index_stage(wl)
+
+
+def test_index_zero_keys_tie_break():
+    # all-zero raw keys: every compressed key is zero (the norm floor), every score
+    # is 0, and the 512 lowest block indices are kept
+    wl = synth.make_workload("dup", "decode", 307, [12000])
+    for b in range(wl.batch):
+        wl.raw_idx_k[b][:] = 0
+    _check_index_stage(wl)
+
+
+# ------------------------------------------------------------------ stage 3 (fed oracle positions)
+
+def _upload_oracle_positions(dw, res, rows):
+    sp = np.full(dw.sel_pos.shape, -1, dtype=np.int32)
+    sc = np.zeros(dw.sel_count.shape, dtype=np.int32)
+    for t in rows:
+        pos = res[t]["positions"]
+        sp[t, :len(pos)] = pos
+        sc[t] = len(pos)
+    dw.sel_pos.copy_(torch.from_numpy(sp))
+    dw.sel_count.copy_(torch.from_numpy(sc))
+
+
+def _check_attention_stage(wl, sample=None):
+    dw = _device(wl)
+    rows = _rows(wl, sample)
+    res = O.run_queries(wl, rows)
+    _upload_oracle_positions(dw, res, range(wl.total_q) if sample is None else rows)
+    dw.attend()
+    torch.cuda.synchronize()
+    out = dw.out_f64()
+    lse = dw.lse.cpu().numpy()
+    worst = 0.0
+    for t in rows:
+        mx, _, _ = P.check_attention(out[t], lse[t], res[t], f"{wl.name} row {t}")
+        worst = max(worst, mx)
+    P.log(f"[attn] {wl.name}: {len(rows)} rows, worst max-abs {worst:.2e}")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_attention_stage_small(name):
+    _check_attention_stage(small(name))
+
+
+@pytest.mark.parametrize("name", list(synth.FULL_SIZE))
+def test_attention_stage_full(name):
+    wl = full(name)
+    _check_attention_stage(wl, sample=48 if wl.kind == "prefill" else None)
+
+
+# ------------------------------------------------------------------ end to end
+
+def _check_e2e(wl, sample=None):
+    dw = _device(wl)
+    dw.build_prefix()
+    dw.step()
+    torch.cuda.synchronize()
+    states = P.oracle_index_states(wl)
+    P.check_comp_cache(wl, dw.comp_numpy(), states)
+    rows = _rows(wl, sample)
+    res = O.run_queries(wl, rows)
+    gb = dw.sel_blocks.cpu().numpy()
+    gp = dw.sel_pos.cpu().numpy()
+    gc = dw.sel_count.cpu().numpy()
+    out = dw.out_f64()
+    lse = dw.lse.cpu().numpy()
+    differing = 0
+    for t in rows:
+        where = f"{wl.name} row {t}"
+        if P.check_selection(gb[t], res[t], where):
+            P.check_positions(gp[t], int(gc[t]), res[t], where)
+            P.check_attention(out[t], lse[t], res[t], where)
+        else:
+            differing += 1
+            P.check_positions_valid(gp[t], int(gc[t]), gb[t], int(wl.q_pos[t]), where)
+    assert differing <= max(1, len(rows) // 50), f"{differing} rows with tie-swapped selections"
+    P.log(f"[e2e] {wl.name}: {len(rows)} rows, {differing} tie-swapped")
+    return dw
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_end_to_end_small(name):
+    _check_e2e(small(name))
+
+
+@pytest.mark.parametrize("name", list(synth.FULL_SIZE))
+def test_end_to_end_full(name):
+    wl = full(name)
+    _check_e2e(wl, sample=48 if wl.kind == "prefill" else None)
+
+
+def test_planted_hot_blocks_selected_on_gpu():
+    wl = full("decode_b8_l32k")
+    dw = _device(wl)
+    dw.build_prefix()
+    dw.step()
+    torch.cuda.synchronize()
+    gb = dw.sel_blocks.cpu().numpy()
+    for b in range(wl.batch):
+        assert np.all(np.isin(wl.hot_blocks[b], gb[b]))
+
+
+# ------------------------------------------------------------------ IndexShare
+
+def _check_indexshare(wl):
+    dw = _device(wl)
+    dw.build_prefix()
+    dw.step()                     # capture: the indexer runs on the last accepted token
+    torch.cuda.synchronize()
+    cap = O.run_queries(wl)
+    res = O.run_indexshare(wl, cap)
+    gb = dw.sel_blocks.cpu().numpy()
+    # reuse steps over the oracle's captured selection (stage isolated)
+    _upload_oracle_positions(dw, cap, range(wl.batch))
+    for j in range(1, wl.reuse_steps + 1):
+        dw.set_reuse(j)
+        dw.reuse_step(j)
+        torch.cuda.synchronize()
+        out = dw.out_f64()
+        lse = dw.lse.cpu().numpy()
+        for b in range(wl.batch):
+            P.check_attention(out[b], lse[b], res[(j, b)], f"{wl.name} reuse step {j} request {b}")
+    for b in range(wl.batch):
+        P.check_selection(gb[b], cap[b], f"{wl.name} capture {b}")
+    P.log(f"[indexshare] {wl.name}: {wl.reuse_steps} reuse steps x {wl.batch} requests")
+
+
+def test_indexshare_small():
+    _check_indexshare(small("indexshare_small"))
+
+
+def test_indexshare_full():
+    _check_indexshare(full("indexshare_b4_l262140"))
+
+
+# ------------------------------------------------------------------ edge cases
+
+def test_max_context():
+    # p = 262143: 65536 visible blocks, the largest the library supports
+    wl = synth.make_workload("maxctx", "decode", 308, [262144], hot_per_req=16)
+    _check_e2e(wl)
+
+
+def test_repeat_runs_are_bitwise_identical():
+    wl = full("decode_b32_loguniform_4k_128k")
+    dw = _device(wl)
+    dw.build_prefix()
+    dw.step()
+    torch.cuda.synchronize()
+    first = [x.clone() for x in (dw.comp, dw.sel_blocks, dw.sel_pos, dw.sel_count, dw.out, dw.lse)]
+    dw.step()
+    torch.cuda.synchronize()
+    for a, b in zip(first, (dw.comp, dw.sel_blocks, dw.sel_pos, dw.sel_count, dw.out, dw.lse)):
+        assert torch.equal(a, b)
