@@ -136,7 +136,7 @@ def build_index_state(raw_bits, length: int, theta: float):
     """
     raw = np.asarray(raw_bits)[:length]
     n_c = length // BLOCK
-    comp = compress_blocks(raw[:BLOCK * n_c].reshape(n_c, BLOCK, -1),
+    comp = compress_blocks(raw[:BLOCK * n_c].reshape(n_c, BLOCK, raw.shape[-1]),
                            BLOCK * np.arange(n_c), theta)
     ring = {t % BLOCK: raw[t].copy() for t in range(BLOCK * n_c, length)}
     return comp, ring
