@@ -130,6 +130,19 @@ class DeviceWorkload:
         """IndexShare reuse step j (after set_reuse(j)): sparse GQA only."""
         self.attend(stream, q=self.reuse_q[j - 1], extra=self.extra, n_extra=4)
 
+    def replicate(self) -> "DeviceWorkload":
+        """An independent device copy of every buffer (same contents, new addresses)."""
+        import copy
+        other = copy.copy(self)
+        for k, v in vars(self).items():
+            if isinstance(v, torch.Tensor) and v.device.type == "cuda":
+                setattr(other, k, v.clone())
+        return other
+
+    def device_bytes(self) -> int:
+        return sum(v.numel() * v.element_size() for v in vars(self).values()
+                   if isinstance(v, torch.Tensor) and v.device.type == "cuda")
+
     # ---------------------------------------------------------------- readback
     def comp_numpy(self) -> np.ndarray:
         return self.comp.cpu().numpy().view(np.uint16)
