@@ -100,7 +100,9 @@ int qsa_index_topk(const qsa_dims* dims, int32_t batch, int32_t total_q, const u
   if (!idx_q || !idx_w || !q_req || !q_pos || !page_table || !comp_cache || !sel_blocks ||
       !sel_pos || !sel_count)
     return QSA_E_NULL;
-  if (!aligned(idx_q, 16) || !aligned(comp_cache, 16)) return QSA_E_SHAPE;
+  if (!aligned(idx_q, 16) || !aligned(comp_cache, 16) || !aligned(sel_pos, 16) ||
+      sel_stride % 4 != 0)
+    return QSA_E_SHAPE;
   const size_t need = qsa::index_workspace_bytes(total_q, max_pos);
   if (!workspace || ws_bytes < need || !aligned(workspace, 256)) return QSA_E_WORKSPACE;
   qsa::IndexArgs a;

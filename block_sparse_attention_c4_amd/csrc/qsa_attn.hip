@@ -40,6 +40,112 @@ __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// Registers of one 32-position step: K rows of the two 16-position tiles and the
+// lane's 8 V rows (both 128-dim halves), plus which of those V rows are real.
+struct KV {
+  u32x4_t k0[8], k1[8];
+  u32x4_t v[2][8];
+  uint32_t okmask;
+};
+
+__device__ __forceinline__ void load_kv(KV& x, const int32_t* s_slot, int cb, int end_local,
+                                        const uint16_t* __restrict__ k_pool,
+                                        const uint16_t* __restrict__ v_pool, int g, int r, int j) {
+  // slot -1 = no position; its loads read slot 0 and are discarded
+  const int li0 = cb + r, li1 = cb + 16 + r;
+  const int s0 = li0 < end_local ? s_slot[li0] : -1;
+  const int s1 = li1 < end_local ? s_slot[li1] : -1;
+  const uint16_t* k0 = k_pool + ((size_t)max(s0, 0) * kKVHeads + g) * kHeadDim + 8 * j;
+  const uint16_t* k1 = k_pool + ((size_t)max(s1, 0) * kKVHeads + g) * kHeadDim + 8 * j;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    x.k0[k] = ld16(k0 + 32 * k);
+    x.k1[k] = ld16(k1 + 32 * k);
+  }
+  uint32_t ok = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int li = cb + (e < 4 ? 0 : 16) + 4 * j + (e & 3);
+    const int sl = li < end_local ? s_slot[li] : -1;
+    ok |= (sl >= 0 ? 1u : 0u) << e;
+    const uint16_t* vp = v_pool + ((size_t)max(sl, 0) * kKVHeads + g) * kHeadDim + 8 * r;
+    x.v[0][e] = ld16(vp);
+    x.v[1][e] = ld16(vp + 128);
+  }
+  x.okmask = ok;
+}
+
+struct SoftmaxState {
+  float m, l;
+  f32x4_t acc[2][8];
+};
+
+__device__ __forceinline__ void attend_step(SoftmaxState& st, const KV& x, const u32x4_t (&qf)[8],
+                                            float scale_log2) {
+  f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    s0 = mfma16(x.k0[k], qf[k], s0);
+    s1 = mfma16(x.k1[k], qf[k], s1);
+  }
+  float xs[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xs[i] = (x.okmask >> i) & 1u ? s0[i] * scale_log2 : -INFINITY;
+    xs[4 + i] = (x.okmask >> (4 + i)) & 1u ? s1[i] * scale_log2 : -INFINITY;
+  }
+  float mx = xs[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) mx = fmaxf(mx, xs[e]);
+  mx = fmaxf(mx, lane_xor16(mx));
+  mx = fmaxf(mx, lane_xor32(mx));
+  const float m_new = fmaxf(st.m, mx);
+  float pr[8];
+  float alpha = 1.f;
+  if (m_new == -INFINITY) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pr[e] = 0.f;
+  } else {
+    alpha = exp2f(st.m - m_new);   // m = -inf gives 0
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pr[e] = exp2f(xs[e] - m_new);
+  }
+  float rs = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) rs += pr[e];
+  rs += lane_xor16(rs);
+  rs += lane_xor32(rs);
+  st.l = st.l * alpha + rs;
+  st.m = m_new;
+  // rows of V that are not real positions are zeroed (their weight is 0, and the
+  // pool may hold anything there)
+  const u32x4_t pf = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                      pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
+#pragma unroll
+  for (int gm = 0; gm < 2; ++gm) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool ok = (x.okmask >> e) & 1u;
+      v[e] = ok ? x.v[gm][e] : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int tau = 0; tau < 8; ++tau) {
+      const uint32_t sel = (tau & 1) ? 0x07060302u : 0x05040100u;
+      const int dw = tau >> 1;
+      u32x4_t a;
+      a.x = __builtin_amdgcn_perm(v[1][dw], v[0][dw], sel);
+      a.y = __builtin_amdgcn_perm(v[3][dw], v[2][dw], sel);
+      a.z = __builtin_amdgcn_perm(v[5][dw], v[4][dw], sel);
+      a.w = __builtin_amdgcn_perm(v[7][dw], v[6][dw], sel);
+      const f32x4_t c = st.acc[gm][tau] * alpha;
+      st.acc[gm][tau] = mfma16(a, pf, c);
+    }
+  }
+}
+
+constexpr int kMaxSplitLen = 2176;   // >= kMaxSel + QSA_MAX_EXTRA, a multiple of 128
+
 __global__ void __launch_bounds__(kThreads)
 attn_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ q_req,
             const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
@@ -51,142 +157,68 @@ attn_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ q_req,
   __shared__ float s_m[kWaves][kGroup];
   __shared__ float s_l[kWaves][kGroup];
   __shared__ float s_acc[kWaves][kGroup][kAccPad];
+  __shared__ int32_t s_slot[kMaxSplitLen];
 
   const int bid = blockIdx.x;
   const int sp = bid % splits;
   const int tg = bid / splits;
   const int g = tg % kKVHeads;
   const int t = tg / kKVHeads;
-  const int req = q_req ? q_req[t] : t;
-  const int cnt = sel_count[t];
-  const int total = cnt + n_extra;
-  const int start = sp * split_len;
-  const int end = min(start + split_len, total);
-
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
   const int r = lane & 15;
   const int j = lane >> 4;
 
-  const int32_t* pt_row = page_table + (size_t)req * pt_stride;
-  const int32_t* lst = sel_pos + (size_t)t * sel_stride;
-  const int32_t* ext = extra_pos ? extra_pos + (size_t)t * n_extra : nullptr;
-
   // Q^T operand: head r of the group (zero for the 8 padding columns)
   u32x4_t qf[8];
   {
     const uint16_t* qrow = q + ((size_t)t * kQHeads + g * kGroup + (r & 7)) * kHeadDim + 8 * j;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      qf[k] = (r < kGroup) ? ld16(qrow + 32 * k) : u32x4_t{0u, 0u, 0u, 0u};
-    }
+    for (int k = 0; k < 8; ++k) qf[k] = (r < kGroup) ? ld16(qrow + 32 * k) : u32x4_t{0u, 0u, 0u, 0u};
   }
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4_t acc[2][8];
+  // translate this split's positions to pool slots once (-1 = no position)
+  const int req = q_req ? q_req[t] : t;
+  const int cnt = sel_count[t];
+  const int total = cnt + n_extra;
+  const int start = sp * split_len;
+  const int len = max(0, min(split_len, total - start));
+  {
+    const int32_t* pt_row = page_table + (size_t)req * pt_stride;
+    const int32_t* lst = sel_pos + (size_t)t * sel_stride;
+    const int32_t* ext = extra_pos ? extra_pos + (size_t)t * n_extra : nullptr;
+    for (int i = tid; i < len; i += kThreads) {
+      const int li = start + i;
+      const int p = li < cnt ? lst[li] : ext[li - cnt];
+      s_slot[i] = p >= 0 ? (int32_t)token_slot(pt_row, p, page_size) : -1;
+    }
+  }
+  __syncthreads();
+
+  SoftmaxState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
 #pragma unroll
   for (int gm = 0; gm < 2; ++gm)
 #pragma unroll
-    for (int tau = 0; tau < 8; ++tau) acc[gm][tau] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int tau = 0; tau < 8; ++tau) st.acc[gm][tau] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int cb = start + w * kChunk; cb < end; cb += kWaves * kChunk) {
-    // list index -> logical position (-1 = no position)
-    auto pos_at = [&](int i) -> int {
-      if (i >= end) return -1;
-      return i < cnt ? lst[i] : ext[i - cnt];
-    };
-    auto slot_of = [&](int p) -> int64_t { return p >= 0 ? token_slot(pt_row, p, page_size) : 0; };
-
-    // K rows of the two 16-position tiles: rows r and 16 + r
-    const int64_t sk0 = slot_of(pos_at(cb + r));
-    const int64_t sk1 = slot_of(pos_at(cb + 16 + r));
-    // V rows (and the logits this lane holds): positions 4j..4j+3 of each tile
-    int64_t sv[8];
-    bool ok[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int li = cb + (e < 4 ? 0 : 16) + 4 * j + (e & 3);
-      const int p = pos_at(li);
-      ok[e] = p >= 0;
-      sv[e] = slot_of(p);
-    }
-
-    u32x4_t kf0[8], kf1[8];
-    const uint16_t* k0 = k_pool + ((size_t)sk0 * kKVHeads + g) * kHeadDim + 8 * j;
-    const uint16_t* k1 = k_pool + ((size_t)sk1 * kKVHeads + g) * kHeadDim + 8 * j;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      kf0[k] = ld16(k0 + 32 * k);
-      kf1[k] = ld16(k1 + 32 * k);
-    }
-    u32x4_t vr[2][8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint16_t* vp = v_pool + ((size_t)sv[e] * kKVHeads + g) * kHeadDim + 8 * r;
-      vr[0][e] = ld16(vp);
-      vr[1][e] = ld16(vp + 128);
-      if (!ok[e]) {
-        vr[0][e] = u32x4_t{0u, 0u, 0u, 0u};
-        vr[1][e] = u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
-
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      s0 = mfma16(kf0[k], qf[k], s0);
-      s1 = mfma16(kf1[k], qf[k], s1);
-    }
-
-    float x[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = ok[i] ? s0[i] * scale_log2 : -INFINITY;
-      x[4 + i] = ok[4 + i] ? s1[i] * scale_log2 : -INFINITY;
-    }
-    float mx = x[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    float pr[8];
-    float alpha = 1.f;
-    if (m_new == -INFINITY) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pr[e] = 0.f;
-    } else {
-      alpha = exp2f(m_run - m_new);   // m_run = -inf gives 0
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pr[e] = exp2f(x[e] - m_new);
-    }
-    float rs = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) rs += pr[e];
-    rs += shfl_xor_f(rs, 16);
-    rs += shfl_xor_f(rs, 32);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-
-    const u32x4_t pf = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                        pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
-#pragma unroll
-    for (int gm = 0; gm < 2; ++gm) {
-#pragma unroll
-      for (int tau = 0; tau < 8; ++tau) {
-        const uint32_t sel = (tau & 1) ? 0x07060302u : 0x05040100u;
-        const int dw = tau >> 1;
-        u32x4_t a;
-        a.x = __builtin_amdgcn_perm(vr[gm][1][dw], vr[gm][0][dw], sel);
-        a.y = __builtin_amdgcn_perm(vr[gm][3][dw], vr[gm][2][dw], sel);
-        a.z = __builtin_amdgcn_perm(vr[gm][5][dw], vr[gm][4][dw], sel);
-        a.w = __builtin_amdgcn_perm(vr[gm][7][dw], vr[gm][6][dw], sel);
-        f32x4_t c = acc[gm][tau] * alpha;
-        acc[gm][tau] = mfma16(a, pf, c);
-      }
+  // this wave's 32-position steps: w, w + 4, ...; two steps' loads in flight
+  const int stride = kWaves * kChunk;
+  KV A, B;
+  int cb = w * kChunk;
+  if (cb < len) load_kv(A, s_slot, cb, len, k_pool, v_pool, g, r, j);
+  if (cb + stride < len) load_kv(B, s_slot, cb + stride, len, k_pool, v_pool, g, r, j);
+  for (; cb < len; cb += 2 * stride) {
+    attend_step(st, A, qf, scale_log2);
+    if (cb + 2 * stride < len) load_kv(A, s_slot, cb + 2 * stride, len, k_pool, v_pool, g, r, j);
+    if (cb + stride < len) {
+      attend_step(st, B, qf, scale_log2);
+      if (cb + 3 * stride < len) load_kv(B, s_slot, cb + 3 * stride, len, k_pool, v_pool, g, r, j);
     }
   }
+  const float m_run = st.m, l_run = st.l;
 
   // merge the 4 waves.  Lane (r, j) holds head r, dims 128*gm + 32*j + 8*i + tau.
   if (r < kGroup) {
@@ -199,7 +231,7 @@ attn_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ q_req,
 #pragma unroll
       for (int tau = 0; tau < 8; ++tau)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s_acc[w][r][128 * gm + 32 * j + 8 * i + tau] = acc[gm][tau][i];
+        for (int i = 0; i < 4; ++i) s_acc[w][r][128 * gm + 32 * j + 8 * i + tau] = st.acc[gm][tau][i];
   }
   __syncthreads();
 
@@ -214,8 +246,7 @@ attn_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ q_req,
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
       const float mw = s_m[ww][h];
-      if (mw == -INFINITY) continue;
-      const float sc = exp2f(mw - M);
+      const float sc = mw == -INFINITY ? 0.f : exp2f(mw - M);
       L += sc * s_l[ww][h];
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] += sc * s_acc[ww][h][d0 + e];
@@ -256,25 +287,23 @@ combine_kernel(const float* __restrict__ part, int splits, uint16_t* __restrict_
   float M = -INFINITY;
   for (int s = 0; s < splits; ++s) {
     const float* pp = base + (size_t)s * kPartFloats;
-    if (pp[kGroup + h] > 0.f) M = fmaxf(M, pp[h]);
+    M = fmaxf(M, pp[kGroup + h] > 0.f ? pp[h] : -INFINITY);
   }
   float L = 0.f;
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (M != -INFINITY) {
-    for (int s = 0; s < splits; ++s) {
-      const float* pp = base + (size_t)s * kPartFloats;
-      const float ls = pp[kGroup + h];
-      if (!(ls > 0.f)) continue;
-      const float sc = exp2f(pp[h] - M);
-      L += sc * ls;
-      const float* pa = pp + 2 * kGroup + h * kHeadDim + d0;
-      const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(pa);
-      const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(pa + 4);
+  for (int s = 0; s < splits; ++s) {
+    const float* pp = base + (size_t)s * kPartFloats;
+    const float ls = pp[kGroup + h];
+    const float* pa = pp + 2 * kGroup + h * kHeadDim + d0;
+    const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(pa);
+    const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(pa + 4);
+    // an empty split wrote l = 0 and zero accumulators: its weight is 0
+    const float sc = (ls > 0.f) ? exp2f(pp[h] - M) : 0.f;
+    L += sc * ls;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o[e] += sc * a0[e];
-        o[4 + e] += sc * a1[e];
-      }
+    for (int e = 0; e < 4; ++e) {
+      o[e] += sc * a0[e];
+      o[4 + e] += sc * a1[e];
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -292,7 +321,7 @@ void attn_plan(int total_q, int n_extra, int* splits, int* split_len) {
   const int bound = kMaxSel + n_extra;
   const int step = kWaves * kChunk;                    // 128 positions
   const int pairs = total_q * kKVHeads;
-  int s = (1024 + pairs - 1) / pairs;
+  int s = (256 + pairs - 1) / pairs;     // about one 4-wave work group per CU
   s = std::max(1, std::min(s, (bound + step - 1) / step));
   int len = (bound + s - 1) / s;
   len = ((len + step - 1) / step) * step;

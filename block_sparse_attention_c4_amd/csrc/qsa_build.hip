@@ -11,21 +11,28 @@
 // 64+4j..64+4j+3, so every rotation is lane local.  The mean is taken in FP32 in
 // token order (as the pages fix); the norm, the rotation and the rounding are
 // done in FP64, which keeps the phase exact to well below a bf16 step even at
-// position 262140 (an FP32 angle would be off by up to ~0.016 rad there).
+// position 262140 (an FP32 angle would be off by up to ~0.016 rad there).  The
+// inverse frequencies theta^(-2i/128) come from the host's libm; the angle is
+// reduced to [-pi, pi] with a two-constant Cody-Waite step before sincos.
 #include "qsa_device.h"
 #include "qsa_launch.h"
+
+#include <cmath>
 
 namespace qsa {
 
 namespace {
 
 constexpr int kUnits = 4;   // blocks per work group
+constexpr double kTwoPiHi = 6.283185307179586;          // 2*pi rounded to double
+constexpr double kTwoPiLo = 2.4492935982947064e-16;     // 2*pi - kTwoPiHi
+constexpr double kInvTwoPi = 0.15915494309189535;
 
 __global__ void __launch_bounds__(64)
 build_kernel(const uint16_t* __restrict__ new_k, const int32_t* __restrict__ cu_new,
              const int32_t* __restrict__ len_before, const int32_t* __restrict__ page_table,
              int pt_stride, int page_size, uint16_t* __restrict__ ring,
-             uint16_t* __restrict__ comp, double theta) {
+             uint16_t* __restrict__ comp, RopeTable rope) {
   const int b = blockIdx.y;
   const int off = cu_new[b];
   const int n = cu_new[b + 1] - off;
@@ -37,6 +44,9 @@ build_kernel(const uint16_t* __restrict__ new_k, const int32_t* __restrict__ cu_
   const int j = threadIdx.x & 15;
   const int c = c0 + blockIdx.x * kUnits + unit;
   const bool complete = (kBlock * c + kBlock - 1) < le;
+  const int bpp = page_size / kBlock;   // compressed rows per page
+  int64_t row = 0;
+  if (complete) row = (int64_t)page_table[(size_t)b * pt_stride + c / bpp] * bpp + (c % bpp);
 
   // read phase: FP32 sum in token order, then * 1/4
   float m[8];
@@ -87,9 +97,12 @@ build_kernel(const uint16_t* __restrict__ new_k, const int32_t* __restrict__ cu_
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int i = 4 * j + e;
-    const double inv_freq = pow(theta, -(2.0 * i) / (double)kIdxDim);
+    const double x = pos * rope.inv_freq[i];
+    const double k = rint(x * kInvTwoPi);
+    double red = fma(-k, kTwoPiHi, x);
+    red = fma(-k, kTwoPiLo, red);
     double s, co;
-    sincos(pos * inv_freq, &s, &co);
+    sincos(red, &s, &co);
     const double a = md[e] / nrm;
     const double bv = md[4 + e] / nrm;
     const double y0 = a * co - bv * s;
@@ -97,8 +110,6 @@ build_kernel(const uint16_t* __restrict__ new_k, const int32_t* __restrict__ cu_
     outw[e] = f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
   }
   // outw[e] packs (dim 4j+e, dim 64+4j+e); store dims 4j..4j+3 and 64+4j..+3
-  const int bpp = page_size / kBlock;   // compressed rows per page
-  const int64_t row = (int64_t)page_table[(size_t)b * pt_stride + c / bpp] * bpp + (c % bpp);
   uint16_t* dst = comp + row * kIdxDim;
   u32x2_t lo, hi;
   lo.x = (outw[0] & 0xffffu) | (outw[1] << 16);
@@ -112,11 +123,14 @@ build_kernel(const uint16_t* __restrict__ new_k, const int32_t* __restrict__ cu_
 }  // namespace
 
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream) {
+  RopeTable rope;
+  for (int i = 0; i < kIdxDim / 2; ++i)
+    rope.inv_freq[i] = std::pow((double)a.theta, -(2.0 * i) / (double)kIdxDim);
   // blocks touched by n new tokens starting anywhere: at most n/4 + 2
   const int units = a.max_new / kBlock + 2;
   dim3 grid((units + kUnits - 1) / kUnits, a.batch);
   hipLaunchKernelGGL(build_kernel, grid, dim3(64), 0, stream, a.new_k, a.cu_new, a.len_before,
-                     a.page_table, a.pt_stride, a.page_size, a.ring, a.comp, (double)a.theta);
+                     a.page_table, a.pt_stride, a.page_size, a.ring, a.comp, rope);
   return hipGetLastError();
 }
 

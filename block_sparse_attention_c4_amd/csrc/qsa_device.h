@@ -71,6 +71,55 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// Value of lane ^ 16 / lane ^ 32, on the VALU (gfx950 v_permlane16/32_swap): swapping
+// a register with itself leaves the partner row (half) in one of the two results.
+__device__ __forceinline__ uint32_t lane_xor16_u32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return ((threadIdx.x >> 4) & 1) ? r[0] : r[1];
+}
+__device__ __forceinline__ uint32_t lane_xor32_u32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return ((threadIdx.x >> 5) & 1) ? r[0] : r[1];
+}
+__device__ __forceinline__ float lane_xor16(float v) {
+  return __uint_as_float(lane_xor16_u32(__float_as_uint(v)));
+}
+__device__ __forceinline__ float lane_xor32(float v) {
+  return __uint_as_float(lane_xor32_u32(__float_as_uint(v)));
+}
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, kRowMask, 0xf, false);
+}
+// Inclusive prefix sum over the 64 lanes (DPP: row shifts, then row broadcasts).
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  x += dpp_i<0x111, 0xf>(x);   // row_shr:1
+  x += dpp_i<0x112, 0xf>(x);   // row_shr:2
+  x += dpp_i<0x114, 0xf>(x);   // row_shr:4
+  x += dpp_i<0x118, 0xf>(x);   // row_shr:8
+  x += dpp_i<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+  x += dpp_i<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
+  return x;
+}
+// Max / min of a 32-bit unsigned over the 64 lanes; every lane gets the result.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)dpp_i<0xb1, 0xf>((int)v));
+  v = max(v, (uint32_t)dpp_i<0x4e, 0xf>((int)v));
+  v = max(v, (uint32_t)dpp_i<0x141, 0xf>((int)v));
+  v = max(v, (uint32_t)dpp_i<0x140, 0xf>((int)v));
+  v = max(v, lane_xor16_u32(v));
+  return max(v, lane_xor32_u32(v));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, (uint32_t)dpp_i<0xb1, 0xf>((int)v));
+  v = min(v, (uint32_t)dpp_i<0x4e, 0xf>((int)v));
+  v = min(v, (uint32_t)dpp_i<0x141, 0xf>((int)v));
+  v = min(v, (uint32_t)dpp_i<0x140, 0xf>((int)v));
+  v = min(v, lane_xor16_u32(v));
+  return min(v, lane_xor32_u32(v));
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 __device__ __forceinline__ u32x4_t ld16(const void* p) {

@@ -7,6 +7,10 @@
 
 namespace qsa {
 
+struct RopeTable {
+  double inv_freq[64];   // theta^(-2i/128), i < 64
+};
+
 struct BuildArgs {
   int batch, max_new, page_size, pt_stride;
   float theta;
@@ -32,12 +36,12 @@ struct IndexArgs {
   int32_t* sel_count;
   // workspace
   float* scores;       // [total_q, score_stride]
-  float* gmax;         // [total_q, score_stride / 16]
   int score_stride;    // multiple of 64, >= max_pos / 4
 };
 size_t index_workspace_bytes(int total_q, int max_pos);
 void index_workspace_carve(IndexArgs& a, void* ws);
 hipError_t launch_index(const IndexArgs& a, hipStream_t stream);
+void launch_topk(const IndexArgs& a, hipStream_t stream);
 
 struct AttnArgs {
   int total_q, page_size, pt_stride, sel_stride, n_extra;

@@ -1,0 +1,392 @@
+// Stage 2b: top-512 block selection and expansion to token positions.
+//
+// [SGLang day-0 post on Qwen3.8-Flash-Next, section "Qwen Sparse Attention:
+// Retrieve Coarsely, Attend Precisely"]: the best 512 blocks are kept, expanded to
+// their 2048 token positions, and the 0..3 tokens of the unfinished block are
+// appended.  Ties go to the lower block index; kept blocks are listed ascending.
+//
+// One 1024-thread work group per query, on an order-preserving 32-bit key of each
+// FP32 score.  With one work group per query the kernel is bound by the length of a
+// thread's instruction stream, so the work is spread over 16 waves and every score
+// of the row is read once, as float4 quads kept in registers (at most 16 quads per
+// thread for 65536 blocks).
+//
+//  1. n <= 512: every block is kept.
+//  2. Lower bound: the 512th largest quad maximum t0 (found to 16 bits below the
+//     keys' common prefix, rounded down) has at least 512 quads, hence 512 scores,
+//     at or above it.  (Skipped when n <= 4096: t0 = 0.)
+//  3. Scores >= t0 go to LDS as candidates (a block-wide prefix count gives their
+//     slots); typically a thousand or fewer.
+//  4. Exact radix select over the candidates: the threshold key and how many keys
+//     equal to it are kept (ties go to the lowest block indices).
+//  5. Kept blocks are marked in an LDS bitmap and written in index order from a
+//     per-word prefix count.
+// Radix passes use 8-bit digits that start at the first bit where the keys' max
+// and min differ; one wave scans the 256-bin histogram while the other waves clear
+// the next one.  More than kCap candidates (heavy ties) falls back to a select over
+// the score row in global memory.
+#include "qsa_device.h"
+#include "qsa_launch.h"
+
+namespace qsa {
+
+namespace {
+
+constexpr int kT = 1024;               // threads per work group
+constexpr int kW = kT / 64;
+constexpr int kCap = 4096;             // LDS candidates
+constexpr int kWords = kMaxBlocks / 32;   // 2048 bitmap words, 2 per thread
+
+struct __attribute__((aligned(16))) Smem {
+  uint32_t red[2 * kW];
+  int wsum[kW];
+  uint32_t hist[2][256];
+  uint32_t key[kCap];
+  uint16_t idx[kCap];
+  uint32_t bits[kWords];
+  uint32_t eqbits[kWords];
+  uint16_t wpre[kWords];               // kept bits in the words before each word
+  int misc[4];
+};
+
+__shared__ Smem sm;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Exclusive scan of one int per thread; .x = prefix, .y = total.
+__device__ __forceinline__ int2 block_scan(int v) {
+  const int w = threadIdx.x >> 6;
+  const int inc = wave_inclusive_sum(v);
+  if (lane_id() == 63) sm.wsum[w] = inc;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kW / 4; ++i) {
+    const int4 x = reinterpret_cast<const int4*>(sm.wsum)[i];
+    const int xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      before += 4 * i + j < w ? xs[j] : 0;
+      all += xs[j];
+    }
+  }
+  __syncthreads();
+  return make_int2(before + inc - v, all);
+}
+
+// One radix-select pass over a histogram that has been filled: wave 0 finds the
+// bin of the kk-th largest, the other waves clear the other histogram.
+__device__ __forceinline__ void radix_find(int buf, int kk) {
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    int mine = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mine += (int)sm.hist[buf][4 * tid + q];
+    const int inc = wave_inclusive_sum(mine);
+    int above = __builtin_amdgcn_readlane(inc, 63) - inc;
+    if (above < kk && kk <= above + mine) {
+      for (int q = 3; q >= 0; --q) {
+        const int h = (int)sm.hist[buf][4 * tid + q];
+        if (kk <= above + h) {
+          sm.misc[0] = 4 * tid + q;
+          sm.misc[1] = kk - above;
+          break;
+        }
+        above += h;
+      }
+    }
+  } else if (tid < 64 + 256) {
+    sm.hist[buf ^ 1][tid - 64] = 0u;
+  }
+}
+
+// k-th largest among the register-held keys (0 = empty).  Returns (key, number of
+// keys equal to it that are kept).  With lower_bound, stops after two digits and
+// returns the lower edge of the bin (at least k keys are >= it).
+template <int E>
+__device__ uint2 select_keys(const uint32_t (&key)[E], int kk, bool lower_bound) {
+  const int tid = threadIdx.x, w = tid >> 6;
+  uint32_t mx = 0u, mn = 0xffffffffu;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    mx = max(mx, key[e]);
+    mn = min(mn, key[e] ? key[e] : 0xffffffffu);
+  }
+  mx = wave_max_u32(mx);
+  mn = wave_min_u32(mn);
+  if (lane_id() == 0) {
+    sm.red[w] = mx;
+    sm.red[kW + w] = mn;
+  }
+  if (tid < 256) sm.hist[0][tid] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kW / 4; ++i) {
+    const uint4 a = reinterpret_cast<const uint4*>(sm.red)[i];
+    const uint4 b = reinterpret_cast<const uint4*>(sm.red + kW)[i];
+    mx = max(max(mx, max(a.x, a.y)), max(a.z, a.w));
+    mn = min(min(mn, min(b.x, b.y)), min(b.z, b.w));
+  }
+  if (mx == mn) return make_uint2(mx, (uint32_t)kk);   // all equal: every kept key ties
+  int hi = 31 - __clz(mx ^ mn);
+  uint32_t prefix = hi == 31 ? 0u : (mx & ~((2u << hi) - 1u));
+  int buf = 0, passes = 0;
+  while (hi >= 0) {
+    const int lo = max(hi - 7, 0);
+    const uint32_t pmask = hi == 31 ? 0u : ~((2u << hi) - 1u);
+    const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint32_t k = key[e];
+      if (k && (k & pmask) == prefix) atomicAdd(&sm.hist[buf][(k >> lo) & dmask], 1u);
+    }
+    __syncthreads();
+    radix_find(buf, kk);
+    __syncthreads();
+    prefix |= (uint32_t)sm.misc[0] << lo;
+    kk = sm.misc[1];
+    buf ^= 1;
+    hi = lo - 1;
+    if (lower_bound && ++passes == 2) break;
+  }
+  return make_uint2(prefix, (uint32_t)kk);
+}
+
+// Slow path for heavy ties: exact k-th largest over the score row in global memory.
+__device__ uint2 select_row(const float* srow, int n, int kk) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t pmask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
+    if (tid < 256) sm.hist[0][tid] = 0u;
+    __syncthreads();
+    for (int i = tid; i < n; i += kT) {
+      const uint32_t key = float_key(srow[i]);
+      if ((key & pmask) == prefix) atomicAdd(&sm.hist[0][(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    radix_find(0, kk);
+    __syncthreads();
+    prefix |= (uint32_t)sm.misc[0] << shift;
+    kk = sm.misc[1];
+  }
+  return make_uint2(prefix, (uint32_t)kk);
+}
+
+// Quads q = tid*E + e of the row (E consecutive quads per thread).  kHold keeps
+// their keys in registers (up to 8 quads per thread); otherwise only the maxima
+// are kept and the row is read again (from L2) for the count and the write.  The
+// lower bound uses the maxima of single quads when n <= 8192, else of 16-block
+// groups (4 quads of a thread), so it ranks at most 2048 / 4096 keys.
+template <int E, bool kHold>
+__device__ void topk_quads(const float* srow, int n) {
+  const int tid = threadIdx.x;
+  const int nq = (n + 3) / 4;
+  auto quad_keys = [&](int e, uint32_t (&k)[4]) {
+    const int q = tid * E + e;
+    const f32x4_t v = q < nq ? *reinterpret_cast<const f32x4_t*>(srow + 4 * q)
+                             : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) k[i] = (4 * q + i < n) ? float_key(v[i]) : 0u;   // 0: past n
+  };
+  uint32_t k4[kHold ? E : 1][4];
+  uint32_t qm[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    uint32_t k[4];
+    quad_keys(e, k);
+    qm[e] = max(max(k[0], k[1]), max(k[2], k[3]));
+    if (kHold)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) k4[kHold ? e : 0][i] = k[i];
+  }
+  uint32_t t0 = 1u;                    // any score qualifies when n <= 4096
+  if (n > 8192) {
+    uint32_t gm[E / 4];
+#pragma unroll
+    for (int g = 0; g < E / 4; ++g)
+      gm[g] = max(max(qm[4 * g], qm[4 * g + 1]), max(qm[4 * g + 2], qm[4 * g + 3]));
+    t0 = max(select_keys<E / 4>(gm, kTopK, true).x, 1u);
+  } else if (n > 4096) {
+    t0 = max(select_keys<E>(qm, kTopK, true).x, 1u);
+  }
+
+  int cnt = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (qm[e] < t0) continue;
+    uint32_t k[4];
+    if (kHold) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) k[i] = k4[kHold ? e : 0][i];
+    } else {
+      quad_keys(e, k);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cnt += k[i] >= t0 ? 1 : 0;
+  }
+  const int2 sc = block_scan(cnt);
+  int off = sc.x;
+  if (sc.y <= kCap) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (qm[e] < t0) continue;
+      uint32_t k[4];
+      if (kHold) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) k[i] = k4[kHold ? e : 0][i];
+      } else {
+        quad_keys(e, k);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (k[i] >= t0) {
+          sm.key[off] = k[i];
+          sm.idx[off] = (uint16_t)(4 * (tid * E + e) + i);
+          ++off;
+        }
+    }
+  }
+  if (tid == 0) sm.misc[2] = sc.y;
+  __syncthreads();
+}
+
+__global__ void __launch_bounds__(kT)
+topk_kernel(const float* __restrict__ scores, int score_stride, const int32_t* __restrict__ q_pos,
+            int32_t* __restrict__ sel_blocks, int32_t* __restrict__ sel_pos, int sel_stride,
+            int32_t* __restrict__ sel_count) {
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int p = q_pos[t];
+  const int n = (p + 1) / kBlock;
+  const int pend = (p + 1) % kBlock;
+  int32_t* row_b = sel_blocks + (size_t)t * kTopK;
+  int32_t* row_p = sel_pos + (size_t)t * sel_stride;
+
+  if (n <= kTopK) {
+    for (int i = tid; i < kTopK; i += kT) row_b[i] = i < n ? i : -1;
+    for (int i = tid; i < sel_stride; i += kT) row_p[i] = i <= p ? i : -1;
+    if (tid == 0) sel_count[t] = p + 1;
+    return;
+  }
+
+  const float* srow = scores + (size_t)t * score_stride;
+  const int nwords = (n + 31) / 32;
+  const int w0 = 2 * tid;              // this thread's two bitmap words
+  if (w0 < nwords) {
+    sm.bits[w0] = 0u;
+    sm.eqbits[w0] = 0u;
+  }
+  if (w0 + 1 < nwords) {
+    sm.bits[w0 + 1] = 0u;
+    sm.eqbits[w0 + 1] = 0u;
+  }
+
+  // candidates (scores >= a lower bound of the 512th) -> sm.key / sm.idx
+  const int nq = (n + 3) / 4;
+  if (nq <= 4 * kT) topk_quads<4, true>(srow, n);
+  else if (nq <= 8 * kT) topk_quads<8, true>(srow, n);
+  else topk_quads<16, false>(srow, n);
+
+  // exact select over the candidates, mark kept (bits) and tied (eqbits) blocks
+  const int ncand = sm.misc[2];
+  uint2 thr;
+  if (ncand <= kCap) {
+    constexpr int EC = kCap / kT;
+    uint32_t ck[EC];
+#pragma unroll
+    for (int e = 0; e < EC; ++e) {
+      const int i = tid + kT * e;
+      ck[e] = i < ncand ? sm.key[i] : 0u;
+    }
+    thr = select_keys<EC>(ck, kTopK, false);
+#pragma unroll
+    for (int e = 0; e < EC; ++e) {
+      const int i = tid + kT * e;
+      if (i < ncand && ck[e] >= thr.x) {
+        const int c = sm.idx[i];
+        atomicOr(ck[e] > thr.x ? &sm.bits[c >> 5] : &sm.eqbits[c >> 5], 1u << (c & 31));
+      }
+    }
+  } else {
+    thr = select_row(srow, n, kTopK);
+    for (int c = tid; c < n; c += kT) {
+      const uint32_t k = float_key(srow[c]);
+      if (k >= thr.x) atomicOr(k > thr.x ? &sm.bits[c >> 5] : &sm.eqbits[c >> 5], 1u << (c & 31));
+    }
+  }
+  __syncthreads();
+
+  // ties: keep the need_eq lowest indices of eqbits (all of them in the usual case)
+  {
+    const int need_eq = (int)thr.y;
+    const uint32_t e0 = w0 < nwords ? sm.eqbits[w0] : 0u;
+    const uint32_t e1 = w0 + 1 < nwords ? sm.eqbits[w0 + 1] : 0u;
+    const int2 es = block_scan(__popc(e0) + __popc(e1));
+    if (es.y == need_eq) {
+      if (e0) sm.bits[w0] |= e0;
+      if (e1) sm.bits[w0 + 1] |= e1;
+    } else {
+      int r = es.x;
+      uint32_t keep0 = 0, keep1 = 0;
+      for (uint32_t e = e0; e; e &= e - 1) keep0 |= (r++ < need_eq) ? (e & (~e + 1u)) : 0u;
+      for (uint32_t e = e1; e; e &= e - 1) keep1 |= (r++ < need_eq) ? (e & (~e + 1u)) : 0u;
+      if (keep0) sm.bits[w0] |= keep0;
+      if (keep1) sm.bits[w0 + 1] |= keep1;
+    }
+  }
+
+  // emit the kept blocks in index order, each expanded to its 4 positions
+  {
+    const uint32_t b0 = w0 < nwords ? sm.bits[w0] : 0u;
+    const uint32_t b1 = w0 + 1 < nwords ? sm.bits[w0 + 1] : 0u;
+    const int idx0 = block_scan(__popc(b0) + __popc(b1)).x;
+    if (n <= 8 * kT) {
+      // dense rows: per-word prefix in LDS, then one block per thread per step
+      if (w0 < nwords) sm.wpre[w0] = (uint16_t)idx0;
+      if (w0 + 1 < nwords) sm.wpre[w0 + 1] = (uint16_t)(idx0 + __popc(b0));
+      __syncthreads();
+      for (int c = tid; c < n; c += kT) {
+        const uint32_t wv = sm.bits[c >> 5];
+        const int b = c & 31;
+        if ((wv >> b) & 1u) {
+          const int idx = sm.wpre[c >> 5] + __popc(wv & ((1u << b) - 1u));
+          if (idx < kTopK) {   // exactly kTopK bits are set; the guard only bounds the row
+            row_b[idx] = c;
+            *reinterpret_cast<int4*>(row_p + kBlock * idx) = make_int4(4 * c, 4 * c + 1, 4 * c + 2, 4 * c + 3);
+          }
+        }
+      }
+    } else {
+      int idx = idx0;
+      const uint32_t word[2] = {b0, b1};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        for (uint32_t e = word[h]; e; e &= e - 1) {
+          const int c = 32 * (w0 + h) + __ffs(e) - 1;
+          if (idx < kTopK) {
+            row_b[idx] = c;
+            *reinterpret_cast<int4*>(row_p + kBlock * idx) = make_int4(4 * c, 4 * c + 1, 4 * c + 2, 4 * c + 3);
+          }
+          ++idx;
+        }
+      }
+    }
+  }
+  const int base = kBlock * kTopK;
+  for (int i = base + tid; i < sel_stride; i += kT) {
+    const int k = i - base;
+    row_p[i] = k < pend ? kBlock * n + k : -1;
+  }
+  if (tid == 0) sel_count[t] = base + pend;
+}
+
+}  // namespace
+
+void launch_topk(const IndexArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(topk_kernel, dim3(a.total_q), dim3(kT), 0, stream, a.scores, a.score_stride,
+                     a.q_pos, a.sel_blocks, a.sel_pos, a.sel_stride, a.sel_count);
+}
+
+}  // namespace qsa

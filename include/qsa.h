@@ -141,7 +141,8 @@ int qsa_build_index_keys(const qsa_dims* dims, int32_t batch, const uint16_t* ne
  *   max_pos (host)                                 > every q_pos; <= QSA_MAX_CONTEXT
  *   comp_cache                                     as written by the builder
  *   sel_blocks [total_q, 512] int32   out
- *   sel_pos    [total_q, sel_stride] int32 out, sel_stride >= 2051
+ *   sel_pos    [total_q, sel_stride] int32 out; sel_stride >= 2051 and a multiple
+ *              of 4, sel_pos 16-byte aligned
  *   sel_count  [total_q] int32        out
  *   workspace  >= qsa_workspace_bytes(QSA_OP_INDEX_TOPK, total_q, max_pos, 0)
  */

@@ -65,6 +65,8 @@ def test_index_topk_validation():
     assert _topk(idx_q=None) == B.QSA_E_NULL
     assert _topk(sel_count=None) == B.QSA_E_NULL
     assert _topk(sel_stride=2050) == B.QSA_E_SHAPE
+    assert _topk(sel_stride=2053) == B.QSA_E_SHAPE            # rows of 4-position groups
+    assert _topk(sel_pos=FAKE + 4) == B.QSA_E_SHAPE
     assert _topk(max_pos=262145) == B.QSA_E_SHAPE
     assert _topk(max_pos=0) == B.QSA_E_SHAPE
     assert _topk(idx_q=FAKE + 2) == B.QSA_E_SHAPE             # misaligned bf16 rows
