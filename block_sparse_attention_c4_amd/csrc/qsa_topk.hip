@@ -75,36 +75,53 @@ __device__ __forceinline__ int2 block_scan(int v) {
 }
 
 // One radix-select pass over a histogram that has been filled: wave 0 finds the
-// bin of the kk-th largest, the other waves clear the other histogram.
+// bin of the kk-th largest (lane l owns bins 4l..4l+3, read as one 16-byte load),
+// the other waves clear the other histogram.
 __device__ __forceinline__ void radix_find(int buf, int kk) {
   const int tid = threadIdx.x;
   if (tid < 64) {
-    int mine = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) mine += (int)sm.hist[buf][4 * tid + q];
+    const uint4 h = reinterpret_cast<const uint4*>(sm.hist[buf])[tid];
+    const int mine = (int)(h.x + h.y + h.z + h.w);
     const int inc = wave_inclusive_sum(mine);
-    int above = __builtin_amdgcn_readlane(inc, 63) - inc;
+    const int above = __builtin_amdgcn_readlane(inc, 63) - inc;   // keys in higher lanes' bins
     if (above < kk && kk <= above + mine) {
-      for (int q = 3; q >= 0; --q) {
-        const int h = (int)sm.hist[buf][4 * tid + q];
-        if (kk <= above + h) {
-          sm.misc[0] = 4 * tid + q;
-          sm.misc[1] = kk - above;
-          break;
-        }
-        above += h;
-      }
+      const int a3 = above + (int)h.w;
+      const int a2 = a3 + (int)h.z;
+      const int a1 = a2 + (int)h.y;
+      int d, r;
+      if (kk <= a3) { d = 3; r = kk - above; }
+      else if (kk <= a2) { d = 2; r = kk - a3; }
+      else if (kk <= a1) { d = 1; r = kk - a2; }
+      else { d = 0; r = kk - a1; }
+      sm.misc[0] = 4 * tid + d;
+      sm.misc[1] = r;
     }
   } else if (tid < 64 + 256) {
     sm.hist[buf ^ 1][tid - 64] = 0u;
   }
 }
 
+// Count one key into the histogram.
+__device__ __forceinline__ void hist_add(uint32_t* hist, bool ok, uint32_t d) {
+  if (ok) atomicAdd(&hist[d], 1u);
+}
+
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 // k-th largest among the register-held keys (0 = empty).  Returns (key, number of
-// keys equal to it that are kept).  With lower_bound, stops after two digits and
-// returns the lower edge of the bin (at least k keys are >= it).
+// keys equal to it that are kept).  With lower_bound, returns instead a key that at
+// least k keys reach (the lower edge of the first pass's bin).
+//
+// Pass 1 bins the values linearly over [min, max] (256 bins), which spreads any
+// score distribution over the histogram (bins of the key's high bits would pile
+// the bulk of the scores into a few exponent bins and serialize the LDS atomics).
+// The keys in the chosen bin lie between conservative key bounds one bin wider on
+// each side; the exact key is then found by 8-bit radix passes over key - (lower
+// bound) among them.
 template <int E>
-__device__ uint2 select_keys(const uint32_t (&key)[E], int kk, bool lower_bound) {
+__device__ __forceinline__ uint2 select_keys(const uint32_t (&key)[E], int kk, bool lower_bound) {
   const int tid = threadIdx.x, w = tid >> 6;
   uint32_t mx = 0u, mn = 0xffffffffu;
 #pragma unroll
@@ -128,9 +145,33 @@ __device__ uint2 select_keys(const uint32_t (&key)[E], int kk, bool lower_bound)
     mn = min(min(mn, min(b.x, b.y)), min(b.z, b.w));
   }
   if (mx == mn) return make_uint2(mx, (uint32_t)kk);   // all equal: every kept key ties
-  int hi = 31 - __clz(mx ^ mn);
-  uint32_t prefix = hi == 31 ? 0u : (mx & ~((2u << hi) - 1u));
-  int buf = 0, passes = 0;
+
+  // pass 1: linear bins of the value
+  const float fmn = key_float(mn), fmx = key_float(mx);
+  const float scale = 256.f / (fmx - fmn);
+  uint32_t lo_key = mn, hi_key = mx;
+  int bin = -1;                        // keys in play: bin == -1 (all) or linear bin == bin
+  int buf = 0;
+  if (scale > 0.f && scale < 3.0e38f && fmx - fmn < 3.0e38f) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int d = min(255, (int)((key_float(key[e]) - fmn) * scale));
+      hist_add(sm.hist[0], key[e] != 0u, (uint32_t)d);
+    }
+    __syncthreads();
+    radix_find(0, kk);
+    __syncthreads();
+    bin = sm.misc[0];
+    kk = sm.misc[1];
+    buf = 1;
+    if (bin > 0) lo_key = max(mn, float_key(fmn + (float)(bin - 1) / scale));
+    if (bin < 255) hi_key = min(mx, float_key(fmn + (float)(bin + 2) / scale));
+    if (lower_bound) return make_uint2(lo_key, 0u);
+  }
+  // radix passes over r = key - lo_key among the keys in play
+  const uint32_t range = hi_key - lo_key;
+  int hi = range ? 31 - __clz(range) : -1;
+  uint32_t prefix = 0u;
   while (hi >= 0) {
     const int lo = max(hi - 7, 0);
     const uint32_t pmask = hi == 31 ? 0u : ~((2u << hi) - 1u);
@@ -138,7 +179,10 @@ __device__ uint2 select_keys(const uint32_t (&key)[E], int kk, bool lower_bound)
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const uint32_t k = key[e];
-      if (k && (k & pmask) == prefix) atomicAdd(&sm.hist[buf][(k >> lo) & dmask], 1u);
+      bool ok = k != 0u;
+      if (bin >= 0) ok = ok && min(255, (int)((key_float(k) - fmn) * scale)) == bin;
+      const uint32_t r = k - lo_key;
+      hist_add(sm.hist[buf], ok && (r & pmask) == prefix, (r >> lo) & dmask);
     }
     __syncthreads();
     radix_find(buf, kk);
@@ -147,9 +191,9 @@ __device__ uint2 select_keys(const uint32_t (&key)[E], int kk, bool lower_bound)
     kk = sm.misc[1];
     buf ^= 1;
     hi = lo - 1;
-    if (lower_bound && ++passes == 2) break;
+    if (lower_bound) break;
   }
-  return make_uint2(prefix, (uint32_t)kk);
+  return make_uint2(lo_key + prefix, (uint32_t)kk);
 }
 
 // Slow path for heavy ties: exact k-th largest over the score row in global memory.
@@ -174,17 +218,17 @@ __device__ uint2 select_row(const float* srow, int n, int kk) {
   return make_uint2(prefix, (uint32_t)kk);
 }
 
-// Quads q = tid*E + e of the row (E consecutive quads per thread).  kHold keeps
-// their keys in registers (up to 8 quads per thread); otherwise only the maxima
-// are kept and the row is read again (from L2) for the count and the write.  The
-// lower bound uses the maxima of single quads when n <= 8192, else of 16-block
-// groups (4 quads of a thread), so it ranks at most 2048 / 4096 keys.
+// Quads q = tid + kT*e of the row (coalesced: a wave reads 1 KB per load).  kHold
+// keeps their keys in registers (up to 8 quads per thread); otherwise only the
+// maxima are kept and the row is read again (from L2) for the count and the write.
+// The lower bound ranks the maxima of single quads when n <= 8192, else of 16-block
+// groups, whose 4 quads sit in 4 adjacent lanes.
 template <int E, bool kHold>
-__device__ void topk_quads(const float* srow, int n) {
+__device__ __forceinline__ void topk_quads(const float* srow, int n) {
   const int tid = threadIdx.x;
   const int nq = (n + 3) / 4;
   auto quad_keys = [&](int e, uint32_t (&k)[4]) {
-    const int q = tid * E + e;
+    const int q = tid + kT * e;
     const f32x4_t v = q < nq ? *reinterpret_cast<const f32x4_t*>(srow + 4 * q)
                              : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -203,11 +247,14 @@ __device__ void topk_quads(const float* srow, int n) {
   }
   uint32_t t0 = 1u;                    // any score qualifies when n <= 4096
   if (n > 8192) {
-    uint32_t gm[E / 4];
+    uint32_t gm[E];
 #pragma unroll
-    for (int g = 0; g < E / 4; ++g)
-      gm[g] = max(max(qm[4 * g], qm[4 * g + 1]), max(qm[4 * g + 2], qm[4 * g + 3]));
-    t0 = max(select_keys<E / 4>(gm, kTopK, true).x, 1u);
+    for (int e = 0; e < E; ++e) {
+      uint32_t m = max(qm[e], (uint32_t)dpp_i<0xb1, 0xf>((int)qm[e]));   // quad_perm [1,0,3,2]
+      m = max(m, (uint32_t)dpp_i<0x4e, 0xf>((int)m));                   // quad_perm [2,3,0,1]
+      gm[e] = (tid & 3) == 0 ? m : 0u;
+    }
+    t0 = max(select_keys<E>(gm, kTopK, true).x, 1u);
   } else if (n > 4096) {
     t0 = max(select_keys<E>(qm, kTopK, true).x, 1u);
   }
@@ -243,7 +290,7 @@ __device__ void topk_quads(const float* srow, int n) {
       for (int i = 0; i < 4; ++i)
         if (k[i] >= t0) {
           sm.key[off] = k[i];
-          sm.idx[off] = (uint16_t)(4 * (tid * E + e) + i);
+          sm.idx[off] = (uint16_t)(4 * (tid + kT * e) + i);
           ++off;
         }
     }
@@ -290,6 +337,7 @@ topk_kernel(const float* __restrict__ scores, int score_stride, const int32_t* _
   else topk_quads<16, false>(srow, n);
 
   // exact select over the candidates, mark kept (bits) and tied (eqbits) blocks
+  if (tid == 0) sm.misc[3] = 0;        // keys equal to the threshold
   const int ncand = sm.misc[2];
   uint2 thr;
   if (ncand <= kCap) {
@@ -306,6 +354,7 @@ topk_kernel(const float* __restrict__ scores, int score_stride, const int32_t* _
       const int i = tid + kT * e;
       if (i < ncand && ck[e] >= thr.x) {
         const int c = sm.idx[i];
+        if (ck[e] == thr.x) atomicAdd(&sm.misc[3], 1);
         atomicOr(ck[e] > thr.x ? &sm.bits[c >> 5] : &sm.eqbits[c >> 5], 1u << (c & 31));
       }
     }
@@ -313,7 +362,10 @@ topk_kernel(const float* __restrict__ scores, int score_stride, const int32_t* _
     thr = select_row(srow, n, kTopK);
     for (int c = tid; c < n; c += kT) {
       const uint32_t k = float_key(srow[c]);
-      if (k >= thr.x) atomicOr(k > thr.x ? &sm.bits[c >> 5] : &sm.eqbits[c >> 5], 1u << (c & 31));
+      if (k >= thr.x) {
+        if (k == thr.x) atomicAdd(&sm.misc[3], 1);
+        atomicOr(k > thr.x ? &sm.bits[c >> 5] : &sm.eqbits[c >> 5], 1u << (c & 31));
+      }
     }
   }
   __syncthreads();
@@ -323,12 +375,11 @@ topk_kernel(const float* __restrict__ scores, int score_stride, const int32_t* _
     const int need_eq = (int)thr.y;
     const uint32_t e0 = w0 < nwords ? sm.eqbits[w0] : 0u;
     const uint32_t e1 = w0 + 1 < nwords ? sm.eqbits[w0 + 1] : 0u;
-    const int2 es = block_scan(__popc(e0) + __popc(e1));
-    if (es.y == need_eq) {
+    if (sm.misc[3] == need_eq) {
       if (e0) sm.bits[w0] |= e0;
       if (e1) sm.bits[w0 + 1] |= e1;
     } else {
-      int r = es.x;
+      int r = block_scan(__popc(e0) + __popc(e1)).x;
       uint32_t keep0 = 0, keep1 = 0;
       for (uint32_t e = e0; e; e &= e - 1) keep0 |= (r++ < need_eq) ? (e & (~e + 1u)) : 0u;
       for (uint32_t e = e1; e; e &= e - 1) keep1 |= (r++ < need_eq) ? (e & (~e + 1u)) : 0u;
