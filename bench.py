@@ -58,10 +58,11 @@ def source_hash(paths) -> str:
     return h.hexdigest()[:16]
 
 
+_CSRC = "block_sparse_attention_c4_amd/csrc/"
 KERNEL_SOURCES = {
-    "attend": ["block_sparse_attention_c4_amd/csrc/qsa_attn.hip", "block_sparse_attention_c4_amd/csrc/qsa_device.h"],
-    "index": ["block_sparse_attention_c4_amd/csrc/qsa_index.hip", "block_sparse_attention_c4_amd/csrc/qsa_device.h"],
-    "build": ["block_sparse_attention_c4_amd/csrc/qsa_build.hip", "block_sparse_attention_c4_amd/csrc/qsa_device.h"],
+    "attend": [_CSRC + f for f in ("qsa_attn.hip", "qsa_device.h", "qsa_launch.h")],
+    "index": [_CSRC + f for f in ("qsa_index.hip", "qsa_topk.hip", "qsa_device.h", "qsa_launch.h")],
+    "build": [_CSRC + f for f in ("qsa_build.hip", "qsa_device.h", "qsa_launch.h")],
 }
 STAGE_KERNELS = {"build": "build_kernel", "index": "score_kernel + topk_kernel",
                  "attend": "attn_kernel + combine_kernel"}
@@ -226,12 +227,13 @@ def main() -> int:
     achieved = nbytes[dom] / (stage_us[dom] * 1e-6) / 1e9
 
     if args.calib_copy_mib:
+        # one elementwise kernel that reads and writes exactly n bytes: the scale of
+        # the memory counters (FETCH_SIZE / WRITE_SIZE) against a known size
         n = args.calib_copy_mib << 20
-        a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        a = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
         b = torch.empty_like(a)
-        a.fill_(1)
         torch.cuda.synchronize()
-        b.copy_(a)
+        torch.mul(a, 1.0, out=b)
         torch.cuda.synchronize()
 
     value = wl.batch / (ms_per_step * 1e-3)
