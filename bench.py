@@ -1,14 +1,21 @@
 #!/usr/bin/env python3
-"""QSA c4 decode throughput on one MI355X.
+"""QSA c4 hot-path throughput on one MI355X.
 
-Workload: batch 32 decode, context lengths log-uniform in [4096, 131072]
-(seed 1003), 16 query / 2 KV heads of 256, indexer 4 x 128, top-512 blocks,
-paged bf16 K/V (page 64) in one shared pool with interleaved pages.
+Default workload (the headline): batch 32 decode, context lengths log-uniform in
+[4096, 131072] (seed 1003), 16 query / 2 KV heads of 256, indexer 4 x 128,
+top-512 blocks, paged bf16 K/V (page 64) in one shared pool with interleaved
+pages.  --workload picks one of the other seeded workloads instead:
 
-A step is one pass of the whole hot path for the batch: ingest the query token's
-indexer key (builder), score + top-512 + expansion (indexer), sparse GQA.  The
-cached prefix's compressed keys are built once before timing.  Inputs are resident
-in HBM; the timed loop cycles through --sets independent copies of the inputs so
+  decode_b1_l4099, decode_b8_l32k      other decode batches
+  prefill_chunk4096_prefix126976       4096 new tokens on a 126976-token prefix
+  indexshare_b4_l262140                batch 4 at L = 262140: IndexShare reuse steps,
+                                       with full decode steps timed beside them
+
+A step is one pass of the whole hot path for the batch: ingest the step's indexer
+keys (builder), score + top-512 + expansion (indexer), sparse GQA.  A reuse step
+is sparse GQA over the frozen selection plus the drafted positions.  The cached
+prefix's compressed keys are built once before timing.  Inputs are resident in
+HBM; the timed loop cycles through --sets independent copies of the inputs so
 that consecutive steps cannot be served from the 256 MB last-level cache.
 
 Prints one JSON line.  --gpus above 1 is refused: nothing here spans GPUs.
@@ -28,17 +35,59 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-METRIC = "QSA decode tokens/s at 128K ctx (indexer+top-k+sparse GQA); HBM GB/s vs peak"
-WORKLOAD = "decode_b32_loguniform_4k_128k"
+HEADLINE = "decode_b32_loguniform_4k_128k"
 HBM_PEAK_GBPS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_b32_loguniform_4k_128k.json")
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+WORKLOADS = {
+    "decode_b32_loguniform_4k_128k": dict(
+        kind="decode", steps=2000, warmup=50, sets=4,
+        metric="QSA decode tokens/s at 128K ctx (indexer+top-k+sparse GQA); HBM GB/s vs peak",
+        context="log-uniform 4096..131072"),
+    "decode_b8_l32k": dict(kind="decode", steps=2000, warmup=50, sets=4,
+                           metric="QSA decode tokens/s, batch 8 at 32K ctx", context="32768 + U{0..3}"),
+    "decode_b1_l4099": dict(kind="decode", steps=2000, warmup=50, sets=4,
+                            metric="QSA decode tokens/s, batch 1 at 4099 ctx", context="4099"),
+    "prefill_chunk4096_prefix126976": dict(
+        kind="prefill", steps=40, warmup=5, sets=2,
+        metric="QSA chunked-prefill tokens/s, 4096-token chunk on a 126976-token prefix",
+        context="126976 cached + 4096 new"),
+    "indexshare_b4_l262140": dict(
+        kind="indexshare", steps=1000, warmup=20, sets=4,
+        metric="QSA IndexShare reuse-step tokens/s, batch 4 at 262140 ctx (full decode step beside it)",
+        context="262140"),
+}
+
+_CSRC = "block_sparse_attention_c4_amd/csrc/"
+KERNEL_SOURCES = {
+    "attend": [_CSRC + f for f in ("qsa_attn.hip", "qsa_device.h", "qsa_launch.h")],
+    "index": [_CSRC + f for f in ("qsa_index.hip", "qsa_topk.hip", "qsa_prefill.hip", "qsa_device.h",
+                                  "qsa_launch.h")],
+    "build": [_CSRC + f for f in ("qsa_build.hip", "qsa_device.h", "qsa_launch.h")],
+}
+ENTRY = {"build": "qsa_build_index_keys", "index": "qsa_index_topk", "attend": "qsa_sparse_gqa_decode"}
 
 
-def algorithmic_bytes(wl, counts: np.ndarray) -> dict:
-    """Bytes each stage must move (read + write), per step.  Counted: the new
+def stage_kernels(kind: str) -> dict:
+    if kind == "prefill":
+        return {"build": "build_kernel",
+                "index": "score_mfma_kernel + topk_codes_kernel (+ rescore_kernel, topk_queued_kernel)",
+                "attend": "attn_kernel + combine_kernel"}
+    return {"build": "build_kernel", "index": "score_kernel + topk_kernel",
+            "attend": "attn_kernel + combine_kernel"}
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
+# ------------------------------------------------------------------ algorithmic work
+
+def decode_bytes(wl, counts: np.ndarray, n_extra: int = 0) -> dict:
+    """Bytes each decode stage must move (read + write), per step.  Counted: the new
     indexer key, ring and compressed key traffic of the builder; the compressed
     keys of every visible block, the indexer query and weights, and the written
-    selection of the indexer; K and V of every selected position (both KV heads),
+    selection of the indexer; K and V of every attended position (both KV heads),
     the position list, the query and the output of sparse GQA.  Not counted:
     scratch scores, split partials and re-reads."""
     p = wl.q_pos.astype(np.int64)
@@ -46,8 +95,27 @@ def algorithmic_bytes(wl, counts: np.ndarray) -> dict:
     completes = ((p + 1) % 4) == 0
     build = int(np.sum(256 + np.where(completes, 3 * 256 + 256, 256)))
     index = int(np.sum(256 * n_c + 4 * 128 * 2 + 4 * 4 + 512 * 4 + 4 * counts + 4))
-    attend = int(np.sum(2 * 2 * 256 * 2 * counts + 4 * counts + 4 + 16 * 256 * 2 * 2 + 16 * 4))
+    att = counts + n_extra
+    attend = int(np.sum(2 * 2 * 256 * 2 * att + 4 * att + 4 + 16 * 256 * 2 * 2 + 16 * 4))
     return {"build": build, "index": index, "attend": attend, "step": build + index + attend}
+
+
+def prefill_work(wl, counts: np.ndarray) -> dict:
+    """FLOPs of the scorer (4 heads x 128 dims, 2 per multiply-add, for every
+    visible block of every query) and of sparse GQA (QK and PV for 16 heads of 256
+    over every attended position); the bytes of unique inputs and outputs."""
+    p = wl.q_pos.astype(np.int64)
+    n_c = (p + 1) // 4
+    T = wl.total_q
+    score_flops = int(np.sum(n_c) * 4 * 128 * 2)
+    attn_flops = int(np.sum(counts) * 16 * 256 * 2 * 2)
+    n_new = int(np.sum(wl.lengths - wl.prefix_len))
+    build_bytes = n_new * 256 + (n_new // 4) * 256
+    index_bytes = int(256 * np.sum(wl.lengths // 4) + T * (4 * 128 * 2 + 16 + 512 * 4 + 4 * 2051 + 4))
+    attend_bytes = int(2 * 2 * 256 * 2 * np.sum(wl.lengths) + T * (16 * 256 * 2 * 2 + 4 * 2051 + 64))
+    return {"score_flops": score_flops, "attn_flops": attn_flops,
+            "bytes": {"build": build_bytes, "index": index_bytes, "attend": attend_bytes,
+                      "step": build_bytes + index_bytes + attend_bytes}}
 
 
 def source_hash(paths) -> str:
@@ -58,22 +126,13 @@ def source_hash(paths) -> str:
     return h.hexdigest()[:16]
 
 
-_CSRC = "block_sparse_attention_c4_amd/csrc/"
-KERNEL_SOURCES = {
-    "attend": [_CSRC + f for f in ("qsa_attn.hip", "qsa_device.h", "qsa_launch.h")],
-    "index": [_CSRC + f for f in ("qsa_index.hip", "qsa_topk.hip", "qsa_device.h", "qsa_launch.h")],
-    "build": [_CSRC + f for f in ("qsa_build.hip", "qsa_device.h", "qsa_launch.h")],
-}
-STAGE_KERNELS = {"build": "build_kernel", "index": "score_kernel + topk_kernel",
-                 "attend": "attn_kernel + combine_kernel"}
-
-
-def load_traffic(stage: str):
+def load_traffic(workload: str, stage: str):
     """HBM bytes per launch of the stage's kernels from the committed rocprofv3
     counter runs, or None if they were taken on different kernel sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = traffic_file(workload)
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         rec = json.load(f)
     ent = rec.get(stage)
     if not ent:
@@ -82,28 +141,78 @@ def load_traffic(stage: str):
     return ent["bytes_per_launch"] if ent.get("source_hash") == cur else None
 
 
+# ------------------------------------------------------------------ CPU baseline (oracle)
+
+def _oracle_keys_at(O, wl, b: int, prefix_keys, p: int):
+    """A request's compressed keys as a query at p sees them: the prefix keys plus
+    the block the query token completes, if it completes one."""
+    if (p + 1) % 4:
+        return prefix_keys
+    c = p // 4
+    blk = O.compress_blocks(wl.raw_idx_k[b][4 * c:4 * c + 4][None], np.array([4 * c]), wl.rope_theta)
+    return np.concatenate([prefix_keys, blk])
+
+
 def cpu_baseline(wl, seconds: float) -> dict:
-    """The oracle's decode step on the same workload, single-threaded, repeated over
-    the batch until `seconds` have passed (the prefix keys are built untimed)."""
+    """The oracle on the same workload, single-threaded, for about `seconds`: decode
+    queries over the batch, prefill query rows of the chunk, or IndexShare reuse
+    steps.  The prefix keys are built untimed; for prefill the chunk's own
+    compressed keys are built inside the timed region."""
     from threadpoolctl import threadpool_limits
     from oracle import qsa_oracle as O
 
-    prefix = [O.build_index_state(wl.raw_idx_k[b], int(wl.q_pos[b]), wl.rope_theta)[0]
-              for b in range(wl.batch)]
     done = 0
+    scale = 1.0 / 16.0
     with threadpool_limits(limits=1):
+        if wl.kind == "prefill":
+            pre = [O.build_index_state(wl.raw_idx_k[b], int(wl.prefix_len[b]), wl.rope_theta)[0]
+                   for b in range(wl.batch)]
+            t0 = time.perf_counter()
+            comp = []
+            for b in range(wl.batch):
+                c0, c1 = int(wl.prefix_len[b]) // 4, int(wl.lengths[b]) // 4
+                blk = O.compress_blocks(wl.raw_idx_k[b][4 * c0:4 * c1].reshape(-1, 4, 128),
+                                        4 * np.arange(c0, c1), wl.rope_theta)
+                comp.append(np.concatenate([pre[b], blk]))
+            for t in range(wl.total_q):
+                b = int(wl.q_req[t])
+                O.query(comp[b], wl.idx_q[t], wl.idx_w[t], wl.q[t], int(wl.q_pos[t]), wl.page_table[b],
+                        wl.k_pool, wl.v_pool, wl.page_size, scale)
+                done += 1
+                if time.perf_counter() - t0 >= seconds:
+                    break
+            el = time.perf_counter() - t0
+            return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                    "sample": f"the chunk's compressed keys, then the first {done} of its "
+                              f"{wl.total_q} query rows, float64 numpy oracle, {el:.1f} s"}
+        prefix = [O.build_index_state(wl.raw_idx_k[b], int(wl.q_pos[b]), wl.rope_theta)[0]
+                  for b in range(wl.batch)]
+        if wl.kind == "indexshare":
+            cap = {}
+            for b in range(wl.batch):
+                p = int(wl.q_pos[b])
+                cap[b] = O.query(_oracle_keys_at(O, wl, b, prefix[b], p), wl.idx_q[b], wl.idx_w[b],
+                                 wl.q[b], p, wl.page_table[b], wl.k_pool, wl.v_pool, wl.page_size,
+                                 scale)["positions"]
+            t0 = time.perf_counter()
+            while True:
+                for b in range(wl.batch):
+                    j = 1 + done % wl.reuse_steps
+                    O.indexshare_step(cap[b], int(wl.q_pos[b]), j, wl.reuse_q[j - 1, b], wl.page_table[b],
+                                      wl.k_pool, wl.v_pool, wl.page_size, scale)
+                    done += 1
+                el = time.perf_counter() - t0
+                if el >= seconds:
+                    break
+            return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                    "sample": f"{done} IndexShare reuse steps (request x step) of the same workload, "
+                              f"float64 numpy oracle, {el:.1f} s"}
         t0 = time.perf_counter()
         while True:
             for b in range(wl.batch):
                 p = int(wl.q_pos[b])
-                comp = prefix[b]
-                if (p + 1) % 4 == 0:     # the query token completes a block
-                    c = p // 4
-                    blk = O.compress_blocks(wl.raw_idx_k[b][4 * c:4 * c + 4][None], np.array([4 * c]),
-                                            wl.rope_theta)
-                    comp = np.concatenate([comp, blk])
-                O.query(comp, wl.idx_q[b], wl.idx_w[b], wl.q[b], p, wl.page_table[b], wl.k_pool,
-                        wl.v_pool, wl.page_size, 1.0 / 16.0)
+                O.query(_oracle_keys_at(O, wl, b, prefix[b], p), wl.idx_q[b], wl.idx_w[b], wl.q[b], p,
+                        wl.page_table[b], wl.k_pool, wl.v_pool, wl.page_size, scale)
                 done += 1
             el = time.perf_counter() - t0
             if el >= seconds:
@@ -113,18 +222,82 @@ def cpu_baseline(wl, seconds: float) -> dict:
                       f"{wl.batch}) of the same workload, float64 numpy oracle, {el:.1f} s"}
 
 
+# ------------------------------------------------------------------ GPU timing
+
+def capture_graphs(torch, fns, outs, refs):
+    """One hipGraph per callable.  refs[i] is the eager result of fns[i] (in outs[i]);
+    every graph is replayed twice and checked against it."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for fn in fns:
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    graphs = []
+    for fn in fns:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for g, out, ref in zip(graphs, outs, refs):
+        for _ in range(2):
+            out.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), "graph replay differs from the eager result"
+    return graphs
+
+
+def time_loop(torch, run, steps: int, warmup: int) -> float:
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        run(i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def time_stages(torch, sets, stages, K: int) -> dict:
+    """Mean duration (us) of each stage from HIP events recorded on the launch
+    stream; the launches queue behind a spin kernel so the GPU runs them back to
+    back."""
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(int(100e6))
+    for i in range(K):
+        d = sets[i % len(sets)]
+        e = ev[i]
+        e[0].record()
+        for j, (_, fn) in enumerate(stages):
+            fn(d)
+            e[j + 1].record()
+    torch.cuda.synchronize()
+    st = {name: [] for name, _ in stages}
+    st["step"] = []
+    for e in ev:
+        for j, (name, _) in enumerate(stages):
+            st[name].append(e[j].elapsed_time(e[j + 1]))
+        st["step"].append(e[0].elapsed_time(e[-1]))
+    return {k: float(np.mean(v)) * 1e3 for k, v in st.items()}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--sets", type=int, default=4, help="input copies cycled through (cold cache)")
-    ap.add_argument("--stage-steps", type=int, default=200)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--sets", type=int, default=None, help="input copies cycled through (cold cache)")
+    ap.add_argument("--stage-steps", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time plain stream launches")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="also run one device copy of this size (counter calibration)")
+                    help="also run one elementwise kernel over this size (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -133,98 +306,74 @@ def main() -> int:
               "the QSA hot path here has no multi-GPU part.", file=sys.stderr)
         return 2
 
+    cfg = WORKLOADS[args.workload]
+    kind = cfg["kind"]
+    steps = args.steps if args.steps is not None else cfg["steps"]
+    warmup = args.warmup if args.warmup is not None else cfg["warmup"]
+    nsets = args.sets if args.sets is not None else cfg["sets"]
+    K = args.stage_steps if args.stage_steps is not None else min(200, steps)
+
     import torch
     from block_sparse_attention_c4_amd import runner, synth
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     torch.cuda.set_device(0)
-    wl = synth.FULL_SIZE[WORKLOAD]()
+    wl = synth.FULL_SIZE[args.workload]()
     base = runner.DeviceWorkload(wl, "cuda:0")
     base.build_prefix()
     torch.cuda.synchronize()
-    sets = [base] + [base.replicate() for _ in range(args.sets - 1)]
+    sets = [base] + [base.replicate() for _ in range(nsets - 1)]
     for d in sets:
         d.ws_attn.zero_()
     base.step()
     torch.cuda.synchronize()
     counts = base.sel_count.cpu().numpy().astype(np.int64)
     ref_out = base.out.clone()
-    nbytes = algorithmic_bytes(wl, counts)
 
-    # ---------------- headline: whole steps, hipGraph replay (or plain launches)
-    launch = "stream"
-    graphs = None
-    if not args.no_graph:
-        try:
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                for d in sets:
-                    d.step()
-            torch.cuda.current_stream().wait_stream(side)
-            graphs = []
-            for d in sets:
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    d.step()
-                graphs.append(g)
+    def timed(fns, outs, refs):
+        """ms per call of fns (cycled), as hipGraph replays unless --no-graph."""
+        graphs = None
+        if not args.no_graph:
+            try:
+                graphs = capture_graphs(torch, fns, outs, refs)
+            except AssertionError:
+                raise
+            except Exception as exc:  # noqa: BLE001
+                print(f"graph capture unavailable ({exc}); timing stream launches", file=sys.stderr)
+        run = (lambda i: graphs[i % len(graphs)].replay()) if graphs else (lambda i: fns[i % len(fns)]())
+        return time_loop(torch, run, steps, warmup), ("hipgraph" if graphs else "stream")
+
+    # ---------------- whole steps
+    ms_step, launch = timed([d.step for d in sets], [d.out for d in sets], [ref_out] * len(sets))
+    assert torch.equal(sets[(steps - 1) % len(sets)].out, ref_out)
+    stages = [("build", lambda d: d.build_step()), ("index", lambda d: d.index()),
+              ("attend", lambda d: d.attend())]
+    stage_us = time_stages(torch, sets, stages, K)
+
+    # ---------------- IndexShare: reuse steps j = 1..3 cycled over the input copies
+    reuse = None
+    if kind == "indexshare":
+        J = wl.reuse_steps
+        extras = []
+        for j in range(1, J + 1):
+            ex = np.full((wl.batch, 4), -1, dtype=np.int32)
+            for b in range(wl.batch):
+                ex[b, :j] = np.arange(int(wl.q_pos[b]) + 1, int(wl.q_pos[b]) + j + 1)
+            extras.append(torch.from_numpy(ex).to("cuda:0"))
+
+        def reuse_call(d, j):
+            return lambda: d.attend(q=d.reuse_q[j - 1], extra=extras[j - 1], n_extra=4)
+
+        fns = [reuse_call(d, 1 + i % J) for i, d in enumerate(sets)]
+        refs = []
+        for d, fn in zip(sets, fns):
+            fn()
             torch.cuda.synchronize()
-            # every replay must give the eager result
-            for i, g in enumerate(graphs):
-                sets[i].out.zero_()
-                g.replay()
-                torch.cuda.synchronize()
-                assert torch.equal(sets[i].out, ref_out), "graph replay differs from eager step"
-            launch = "hipgraph"
-        except Exception as exc:  # noqa: BLE001
-            print(f"graph capture unavailable ({exc}); timing stream launches", file=sys.stderr)
-            graphs = None
-
-    def run_step(i):
-        if graphs is not None:
-            graphs[i % len(graphs)].replay()
-        else:
-            sets[i % len(sets)].step()
-
-    for i in range(args.warmup):
-        run_step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        run_step(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    torch.cuda.synchronize()
-    assert torch.equal(sets[(args.steps - 1) % len(sets)].out, ref_out)
-
-    # ---------------- per-stage durations: HIP events on the launch stream, queued
-    # behind a spin kernel so the GPU runs the stages back to back
-    K = args.stage_steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    torch.cuda.synchronize()
-    if hasattr(torch.cuda, "_sleep"):
-        torch.cuda._sleep(int(100e6))
-    for i in range(K):
-        d = sets[i % len(sets)]
-        e = ev[i]
-        e[0].record()
-        d.build_step()
-        e[1].record()
-        d.index()
-        e[2].record()
-        d.attend()
-        e[3].record()
-    torch.cuda.synchronize()
-    st = {"build": [], "index": [], "attend": [], "step": []}
-    for e in ev:
-        st["build"].append(e[0].elapsed_time(e[1]))
-        st["index"].append(e[1].elapsed_time(e[2]))
-        st["attend"].append(e[2].elapsed_time(e[3]))
-        st["step"].append(e[0].elapsed_time(e[3]))
-    stage_us = {k: float(np.mean(v)) * 1e3 for k, v in st.items()}
-    dom = max(("build", "index", "attend"), key=lambda k: stage_us[k])
-    achieved = nbytes[dom] / (stage_us[dom] * 1e-6) / 1e9
+            refs.append(d.out.clone())
+        ms_reuse, _ = timed(fns, [d.out for d in sets], refs)
+        rst = time_stages(torch, sets, [("reuse", lambda d: d.attend(
+            q=d.reuse_q[J - 1], extra=extras[J - 1], n_extra=4))], K)
+        reuse = {"ms": ms_reuse, "attend_us": rst["reuse"]}
 
     if args.calib_copy_mib:
         # one elementwise kernel that reads and writes exactly n bytes: the scale of
@@ -236,34 +385,60 @@ def main() -> int:
         torch.mul(a, 1.0, out=b)
         torch.cuda.synchronize()
 
-    value = wl.batch / (ms_per_step * 1e-3)
-    result = {
-        "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": WORKLOAD, "batch": wl.batch, "seed": wl.seed,
-                   "context": "log-uniform 4096..131072", "q_heads": 16, "kv_heads": 2,
-                   "head_dim": 256, "indexer": "4x128", "topk_blocks": 512, "page_size": 64,
-                   "input_sets": len(sets), "launch": launch},
-        "step_hbm_gbps": round(nbytes["step"] / (ms_per_step * 1e-3) / 1e9, 1),
-        "step_hbm_frac": round(nbytes["step"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "algorithmic_bytes": nbytes,
-        "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
-        "roofline": {"bound": "hbm", "kernel": STAGE_KERNELS[dom], "entry_point": {
-            "build": "qsa_build_index_keys", "index": "qsa_index_topk",
-            "attend": "qsa_sparse_gqa_decode"}[dom],
-            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(dom)},
-    }
+    kernels = stage_kernels(kind)
+    config = {"workload": args.workload, "batch": wl.batch, "seed": wl.seed, "context": cfg["context"],
+              "q_heads": 16, "kv_heads": 2, "head_dim": 256, "indexer": "4x128", "topk_blocks": 512,
+              "page_size": wl.page_size, "input_sets": len(sets), "launch": launch}
+    result = {"metric": cfg["metric"], "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+              "warmup": warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": config}
+    result["stage_us"] = {k: round(v, 2) for k, v in stage_us.items()}
+
+    if kind == "prefill":
+        work = prefill_work(wl, counts)
+        config["chunk"] = int(wl.total_q)
+        result["value"] = round(wl.total_q / (ms_step * 1e-3), 1)
+        result["ms_per_step"] = round(ms_step, 5)
+        score_tf = work["score_flops"] / (stage_us["index"] * 1e-6) / 1e12
+        attn_tf = work["attn_flops"] / (stage_us["attend"] * 1e-6) / 1e12
+        result["stage_tflops"] = {"index_scoring": round(score_tf, 1), "attend": round(attn_tf, 1)}
+        result["algorithmic"] = {"score_flops": work["score_flops"], "attn_flops": work["attn_flops"],
+                                 "unique_bytes": work["bytes"]}
+        # the scorer's FLOPs over the whole indexer call (scorer + code select): a
+        # lower bound on the scorer kernel's own rate
+        result["roofline"] = {"bound": "mfma", "kernel": kernels["index"], "entry_point": ENTRY["index"],
+                              "achieved": round(score_tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(score_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                              "traffic": load_traffic(args.workload, "index")}
+    elif kind == "indexshare":
+        nbytes = decode_bytes(wl, counts)
+        att = decode_bytes(wl, counts, n_extra=wl.reuse_steps)["attend"]
+        result["value"] = round(wl.batch / (reuse["ms"] * 1e-3), 1)
+        result["ms_per_step"] = round(reuse["ms"], 5)
+        result["ms_per_step_without_reuse"] = round(ms_step, 5)
+        result["tokens_per_s_without_reuse"] = round(wl.batch / (ms_step * 1e-3), 1)
+        result["reuse_attend_us"] = round(reuse["attend_us"], 2)
+        result["algorithmic_bytes"] = nbytes
+        result["algorithmic_bytes_reuse_step"] = att
+        achieved = att / (reuse["attend_us"] * 1e-6) / 1e9
+        result["roofline"] = {"bound": "hbm", "kernel": kernels["attend"], "entry_point": ENTRY["attend"],
+                              "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                              "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                              "traffic": load_traffic(args.workload, "attend")}
+    else:
+        nbytes = decode_bytes(wl, counts)
+        result["value"] = round(wl.batch / (ms_step * 1e-3), 1)
+        result["ms_per_step"] = round(ms_step, 5)
+        result["step_hbm_gbps"] = round(nbytes["step"] / (ms_step * 1e-3) / 1e9, 1)
+        result["step_hbm_frac"] = round(nbytes["step"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+        result["algorithmic_bytes"] = nbytes
+        dom = max(("build", "index", "attend"), key=lambda k: stage_us[k])
+        achieved = nbytes[dom] / (stage_us[dom] * 1e-6) / 1e9
+        result["roofline"] = {"bound": "hbm", "kernel": kernels[dom], "entry_point": ENTRY[dom],
+                              "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                              "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                              "traffic": load_traffic(args.workload, dom)}
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libqsa.so")
 OBJ = os.path.join(ROOT, "_build")
-SOURCES = ["qsa_api.cpp", "qsa_build.hip", "qsa_index.hip", "qsa_topk.hip", "qsa_attn.hip"]
+SOURCES = ["qsa_api.cpp", "qsa_build.hip", "qsa_index.hip", "qsa_topk.hip", "qsa_prefill.hip",
+           "qsa_attn.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

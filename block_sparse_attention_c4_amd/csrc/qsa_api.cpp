@@ -106,6 +106,7 @@ int qsa_index_topk(const qsa_dims* dims, int32_t batch, int32_t total_q, const u
   const size_t need = qsa::index_workspace_bytes(total_q, max_pos);
   if (!workspace || ws_bytes < need || !aligned(workspace, 256)) return QSA_E_WORKSPACE;
   qsa::IndexArgs a;
+  a.batch = batch;
   a.total_q = total_q;
   a.max_pos = max_pos;
   a.page_size = dims->page_size;

@@ -129,19 +129,39 @@ score_kernel(int nq, const uint16_t* __restrict__ idx_q, const float* __restrict
 
 }  // namespace
 
-size_t index_workspace_bytes(int total_q, int max_pos) {
+// Workspace: FP32 score rows [total_q, stride]; the code rows and group maxima of
+// the MFMA path live in the same bytes (the FP32 rows are written only after every
+// code has been read).  Then the queue of rows handed to the FP32 select.
+static size_t score_rows_bytes(int total_q, int max_pos, int* stride) {
   const int nb = (max_pos + kBlock - 1) / kBlock;
-  const size_t stride = (size_t)((nb + 63) / 64) * 64;
-  return ((size_t)total_q * stride * sizeof(float) + 255) / 256 * 256;
+  *stride = ((nb + 127) / 128) * 128;
+  return ((size_t)total_q * *stride * sizeof(float) + 255) / 256 * 256;
+}
+
+size_t index_workspace_bytes(int total_q, int max_pos) {
+  int stride;
+  const size_t rows = score_rows_bytes(total_q, max_pos, &stride);
+  return rows + ((size_t)(total_q + 1) * sizeof(int) + 255) / 256 * 256;
 }
 
 void index_workspace_carve(IndexArgs& a, void* ws) {
-  const int nb = (a.max_pos + kBlock - 1) / kBlock;
-  a.score_stride = ((nb + 63) / 64) * 64;
-  a.scores = reinterpret_cast<float*>(ws);
+  const size_t rows = score_rows_bytes(a.total_q, a.max_pos, &a.score_stride);
+  char* base = static_cast<char*>(ws);
+  a.scores = reinterpret_cast<float*>(base);
+  a.codes = reinterpret_cast<uint16_t*>(base);
+  a.gmax = a.codes + (size_t)a.total_q * a.score_stride;
+  a.queue = reinterpret_cast<int*>(base + rows);
+}
+
+// Decode-like batches (about one query per request) take the paged GEMV scorer and
+// the latency-oriented select; chunks of many queries per request share their keys
+// and take the MFMA scorer.
+static bool use_mfma(const IndexArgs& a) {
+  return a.total_q >= 64 && a.total_q >= 4 * a.batch;
 }
 
 hipError_t launch_index(const IndexArgs& a, hipStream_t stream) {
+  if (use_mfma(a)) return launch_index_mfma(a, stream);
   constexpr int kQPerLaunch = 64;
   for (int q0 = 0; q0 < a.total_q; q0 += kQPerLaunch) {
     const int nq = std::min(kQPerLaunch, a.total_q - q0);

@@ -24,7 +24,7 @@ struct BuildArgs {
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
 
 struct IndexArgs {
-  int total_q, max_pos, page_size, pt_stride, sel_stride;
+  int batch, total_q, max_pos, page_size, pt_stride, sel_stride;
   const uint16_t* idx_q;
   const float* idx_w;
   const int32_t* q_req;
@@ -35,13 +35,18 @@ struct IndexArgs {
   int32_t* sel_pos;
   int32_t* sel_count;
   // workspace
-  float* scores;       // [total_q, score_stride]
-  int score_stride;    // multiple of 64, >= max_pos / 4
+  float* scores;       // [total_q, score_stride] FP32 scores
+  uint16_t* codes;     // [total_q, score_stride] score codes (aliases scores)
+  uint16_t* gmax;      // [total_q, score_stride / 16] group maxima of the codes (aliases scores)
+  int* queue;          // [1 + total_q]: count, then rows handed to the FP32 select
+  int score_stride;    // multiple of 128, >= max_pos / 4
 };
 size_t index_workspace_bytes(int total_q, int max_pos);
 void index_workspace_carve(IndexArgs& a, void* ws);
 hipError_t launch_index(const IndexArgs& a, hipStream_t stream);
+hipError_t launch_index_mfma(const IndexArgs& a, hipStream_t stream);
 void launch_topk(const IndexArgs& a, hipStream_t stream);
+void launch_topk_queued(const IndexArgs& a, hipStream_t stream);
 
 struct AttnArgs {
   int total_q, page_size, pt_stride, sel_stride, n_extra;

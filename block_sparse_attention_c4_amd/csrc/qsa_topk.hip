@@ -24,7 +24,8 @@
 // Radix passes use 8-bit digits that start at the first bit where the keys' max
 // and min differ; one wave scans the 256-bin histogram while the other waves clear
 // the next one.  More than kCap candidates (heavy ties) falls back to a select over
-// the score row in global memory.
+// the score row in global memory.  topk_queued_kernel runs the same select for the
+// rows that the code-based select of qsa_prefill.hip hands over.
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
@@ -299,11 +300,10 @@ __device__ __forceinline__ void topk_quads(const float* srow, int n) {
   __syncthreads();
 }
 
-__global__ void __launch_bounds__(kT)
-topk_kernel(const float* __restrict__ scores, int score_stride, const int32_t* __restrict__ q_pos,
-            int32_t* __restrict__ sel_blocks, int32_t* __restrict__ sel_pos, int sel_stride,
-            int32_t* __restrict__ sel_count) {
-  const int t = blockIdx.x;
+__device__ __forceinline__ void topk_row(int t, const float* __restrict__ scores, int score_stride,
+                                         const int32_t* __restrict__ q_pos,
+                                         int32_t* __restrict__ sel_blocks, int32_t* __restrict__ sel_pos,
+                                         int sel_stride, int32_t* __restrict__ sel_count) {
   const int tid = threadIdx.x;
   const int p = q_pos[t];
   const int n = (p + 1) / kBlock;
@@ -433,11 +433,37 @@ topk_kernel(const float* __restrict__ scores, int score_stride, const int32_t* _
   if (tid == 0) sel_count[t] = base + pend;
 }
 
+__global__ void __launch_bounds__(kT)
+topk_kernel(const float* __restrict__ scores, int score_stride, const int32_t* __restrict__ q_pos,
+            int32_t* __restrict__ sel_blocks, int32_t* __restrict__ sel_pos, int sel_stride,
+            int32_t* __restrict__ sel_count) {
+  topk_row(blockIdx.x, scores, score_stride, q_pos, sel_blocks, sel_pos, sel_stride, sel_count);
+}
+
+// The rows listed in queue[1 .. queue[0]] (rows the code-based select hands over).
+__global__ void __launch_bounds__(kT)
+topk_queued_kernel(const int* __restrict__ queue, const float* __restrict__ scores,
+                   int score_stride, const int32_t* __restrict__ q_pos,
+                   int32_t* __restrict__ sel_blocks, int32_t* __restrict__ sel_pos, int sel_stride,
+                   int32_t* __restrict__ sel_count) {
+  const int nq = queue[0];
+  for (int k = blockIdx.x; k < nq; k += gridDim.x) {
+    __syncthreads();                   // LDS of the previous row is free
+    topk_row(queue[1 + k], scores, score_stride, q_pos, sel_blocks, sel_pos, sel_stride, sel_count);
+  }
+}
+
 }  // namespace
 
 void launch_topk(const IndexArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(topk_kernel, dim3(a.total_q), dim3(kT), 0, stream, a.scores, a.score_stride,
                      a.q_pos, a.sel_blocks, a.sel_pos, a.sel_stride, a.sel_count);
+}
+
+void launch_topk_queued(const IndexArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(topk_queued_kernel, dim3(std::min(a.total_q, 256)), dim3(kT), 0, stream, a.queue,
+                     a.scores, a.score_stride, a.q_pos, a.sel_blocks, a.sel_pos, a.sel_stride,
+                     a.sel_count);
 }
 
 }  // namespace qsa

@@ -40,8 +40,17 @@ SMALL = {
         hot_per_req=8),
     "decode_page16": lambda: synth.make_workload(
         "decode_page16", "decode", 302, [37, 2060, 9000, 35000], hot_per_req=4, page_size=16),
+    # many queries per request: the MFMA scorer and the code-based select.  A 64-query
+    # tile straddles the two requests; rows of 516..525 blocks take the whole-row
+    # select, rows of ~8330 blocks the group-maximum candidates; 74 rows leave a
+    # ragged last tile
     "prefill_ragged": lambda: synth.make_workload(
         "prefill_ragged", "prefill", 303, [2101, 33333], chunk=37),
+    # page 16 (a 16-block group spans 4 pages), rows with fewer than 512 blocks,
+    # three requests in one tile, ~17500-block rows
+    "prefill_page16_mixed": lambda: synth.make_workload(
+        "prefill_page16_mixed", "prefill", 309, [300, 9000, 70001], chunk=70, page_size=16,
+        hot_per_req=6),
     "indexshare_small": lambda: synth.make_workload(
         "indexshare_small", "indexshare", 304, [4100, 33003, 700], reuse_steps=3),
 }
@@ -167,6 +176,23 @@ def test_index_zero_keys_tie_break():
     wl = synth.make_workload("dup", "decode", 307, [12000])
     for b in range(wl.batch):
         wl.raw_idx_k[b][:] = 0
+    _check_index_stage(wl)
+
+
+def test_index_prefill_all_ties():
+    # many queries, every score 0: each row is handed from the code-based select to
+    # the FP32 select, which keeps the 512 lowest blocks
+    wl = synth.make_workload("ties_prefill", "prefill", 310, [9000, 40000], chunk=48)
+    wl.idx_q[:] = 0
+    _check_index_stage(wl)
+
+
+def test_index_prefill_equal_keys():
+    # every raw key equal: every compressed key of a request differs only by its
+    # rotation, so scores spread over few distinct codes; plus rows with all-zero keys
+    wl = synth.make_workload("eq_prefill", "prefill", 311, [20000, 6000], chunk=40)
+    wl.raw_idx_k[0][:] = wl.raw_idx_k[0][0]
+    wl.raw_idx_k[1][:] = 0
     _check_index_stage(wl)
 
 
