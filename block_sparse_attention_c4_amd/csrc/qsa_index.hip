@@ -36,11 +36,23 @@ __device__ __forceinline__ int groups_of(int p) {
 // One wave per work group.  The (at most 64) queries of a launch are laid out one
 // per lane: each lane holds its query's group count, first group, request and
 // block count, and a group index is mapped to its query with one ballot.  The
-// wave takes a contiguous range of the launch's groups and keeps two groups'
-// loads in flight while it computes the previous one.
-struct GroupLoad {
-  u32x4_t kv[4];
-  int t, g;
+// wave takes a contiguous range of at most kWaveGroups groups.
+//
+// The loop over the range issues loads only: page-table entries two groups ahead,
+// keys (and the query's rows when the query changes) one group ahead, each into a
+// ping-pong register set; scores stay in LDS until the range is done.  With no
+// store in flight the in-order load counter lets each wait cover exactly the loads
+// it needs, so three groups' loads overlap.
+constexpr int kWaveGroups = 64;
+
+struct GroupMeta {
+  int t, g, n_c;
+  const int32_t* pt_row;
+};
+
+struct QueryRows {
+  u32x4_t qf[kIdxHeads];
+  float w[kIdxHeads];
 };
 
 __global__ void __launch_bounds__(64)
@@ -48,6 +60,8 @@ score_kernel(int nq, const uint16_t* __restrict__ idx_q, const float* __restrict
              const int32_t* __restrict__ q_req, const int32_t* __restrict__ q_pos,
              const int32_t* __restrict__ page_table, int pt_stride, int page_size,
              const uint16_t* __restrict__ comp, float* __restrict__ scores, int score_stride) {
+  __shared__ float s_out[kWaveGroups * kScoreGroup];
+  __shared__ int s_tg[kWaveGroups];    // query << 16 | group, per group of the range
   const int lane = threadIdx.x;
   const int my_nc = lane < nq ? (q_pos[lane] + 1) / kBlock : 0;
   const int my_req = lane < nq ? q_req[lane] : 0;
@@ -63,66 +77,112 @@ score_kernel(int nq, const uint16_t* __restrict__ idx_q, const float* __restrict
   const int wave = blockIdx.x, nwaves = gridDim.x;
   const int g_begin = (int)(((int64_t)total * wave) / nwaves);
   const int g_end = (int)(((int64_t)total * (wave + 1)) / nwaves);
-  if (g_begin >= g_end) return;
+  const int ng = g_end - g_begin;      // <= kWaveGroups (the launch sizes the grid for it)
+  if (ng <= 0) return;
 
   const int d0 = (lane & 15) * 8;
   const int row_in_step = lane >> 4;
   const int bpp = page_size / kBlock;
 
-  auto issue = [&](GroupLoad& L, int gi) {
-    const int t = __popcll(__ballot(incl <= gi));   // first query whose groups reach gi
-    L.t = t;
-    L.g = gi - __shfl(excl, t, 64);
-    const int n_c = __shfl(my_nc, t, 64);
-    const int32_t* pt_row = page_table + (size_t)__shfl(my_req, t, 64) * pt_stride;
+  auto meta = [&](int i) {             // group g_begin + i: i wave-uniform, every lane active
+    GroupMeta m;
+    const int gi = g_begin + i;
+    m.t = __popcll(__ballot(incl <= gi));   // first query whose groups reach gi
+    m.g = gi - __shfl(excl, m.t, 64);
+    m.n_c = __shfl(my_nc, m.t, 64);
+    m.pt_row = page_table + (size_t)__shfl(my_req, m.t, 64) * pt_stride;
+    return m;
+  };
+  auto block_of = [&](const GroupMeta& m, int r) {
+    return min(m.g * kScoreGroup + 4 * r + row_in_step, m.n_c - 1);
+  };
+  auto pt_load = [&](int i, int (&pg)[4]) {
+    const GroupMeta m = meta(i);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pg[r] = m.pt_row[block_of(m, r) / bpp];
+  };
+  auto key_load = [&](int i, const int (&pg)[4], u32x4_t (&kv)[4]) {
+    const GroupMeta m = meta(i);
+    if (lane == 0) s_tg[i] = (m.t << 16) | m.g;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int c = min(L.g * kScoreGroup + 4 * r + row_in_step, n_c - 1);
-      const int64_t row = (int64_t)pt_row[c / bpp] * bpp + (c % bpp);
-      L.kv[r] = ld16(comp + row * kIdxDim + d0);
+      const int c = block_of(m, r);
+      const int64_t row = (int64_t)pg[r] * bpp + (c % bpp);
+      kv[r] = ld16(comp + row * kIdxDim + d0);
     }
   };
-
-  int cur_t = -1;
-  u32x4_t qf[kIdxHeads];
-  float w[kIdxHeads];
-  auto compute = [&](const GroupLoad& L) {
-    const int t = L.t;
-    if (t != cur_t) {
-      cur_t = t;
+  auto query_load = [&](int t, QueryRows& q) {
 #pragma unroll
-      for (int h = 0; h < kIdxHeads; ++h) {
-        qf[h] = ld16(idx_q + ((size_t)t * kIdxHeads + h) * kIdxDim + d0);
-        w[h] = idx_w[(size_t)t * kIdxHeads + h];
-      }
+    for (int h = 0; h < kIdxHeads; ++h) {
+      q.qf[h] = ld16(idx_q + ((size_t)t * kIdxHeads + h) * kIdxDim + d0);
+      q.w[h] = idx_w[(size_t)t * kIdxHeads + h];
     }
-    const int n_c = __shfl(my_nc, t, 64);
+  };
+  auto compute = [&](int i, const u32x4_t (&kv)[4], const QueryRows& q) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float s = 0.f;
 #pragma unroll
       for (int h = 0; h < kIdxHeads; ++h) {
-        float a = dot2(L.kv[r].x, qf[h].x, 0.f);
-        a = dot2(L.kv[r].y, qf[h].y, a);
-        a = dot2(L.kv[r].z, qf[h].z, a);
-        a = dot2(L.kv[r].w, qf[h].w, a);
+        float a = dot2(kv[r].x, q.qf[h].x, 0.f);
+        a = dot2(kv[r].y, q.qf[h].y, a);
+        a = dot2(kv[r].z, q.qf[h].z, a);
+        a = dot2(kv[r].w, q.qf[h].w, a);
         a = row16_sum(a);
-        s += w[h] * fmaxf(a, 0.f);
+        s += q.w[h] * fmaxf(a, 0.f);
       }
-      const int c = L.g * kScoreGroup + 4 * r + row_in_step;
-      if (c < n_c && (lane & 15) == 0) scores[(size_t)t * score_stride + c] = s;
+      if ((lane & 15) == 0) s_out[i * kScoreGroup + 4 * r + row_in_step] = s;
     }
   };
 
-  GroupLoad A, B;
-  issue(A, g_begin);
-  if (g_begin + 1 < g_end) issue(B, g_begin + 1);
-  for (int gi = g_begin; gi < g_end; gi += 2) {
-    compute(A);
-    if (gi + 2 < g_end) issue(A, gi + 2);
-    if (gi + 1 < g_end) {
-      compute(B);
-      if (gi + 3 < g_end) issue(B, gi + 3);
+  // pipeline: at step i the page entries of group i+2 and the keys of group i+1 are
+  // requested, then group i is scored
+  int pg0[4], pg1[4];
+  u32x4_t kv0[4], kv1[4];
+  QueryRows q0, q1;
+  int t0 = meta(0).t;
+  query_load(t0, q0);
+  pt_load(0, pg0);
+  if (ng > 1) pt_load(1, pg1);
+  key_load(0, pg0, kv0);
+  int tq1 = t0;
+  for (int i = 0; i < ng; i += 2) {
+    // even step: group i in kv0 / q0
+    if (i + 2 < ng) pt_load(i + 2, pg0);
+    if (i + 1 < ng) {
+      tq1 = meta(i + 1).t;
+      if (tq1 != t0) query_load(tq1, q1); else q1 = q0;
+      key_load(i + 1, pg1, kv1);
+    }
+    compute(i, kv0, q0);
+    if (i + 1 >= ng) break;
+    // odd step: group i+1 in kv1 / q1
+    if (i + 3 < ng) pt_load(i + 3, pg1);
+    if (i + 2 < ng) {
+      t0 = meta(i + 2).t;
+      if (t0 != tq1) query_load(t0, q0); else q0 = q1;
+      key_load(i + 2, pg0, kv0);
+    }
+    compute(i + 1, kv1, q1);
+  }
+
+  // write the range's scores: lane l covers group l / 4, blocks 4 (l % 4) .. +3
+  for (int i0 = 0; i0 < ng; i0 += 16) {
+    const int i = min(i0 + (lane >> 2), ng - 1);
+    const int tg = s_tg[i];
+    const int t = tg >> 16;
+    const int n_c = __shfl(my_nc, t, 64);     // every lane active: its own query's count
+    if (i0 + (lane >> 2) < ng) {
+      const int c = (tg & 0xffff) * kScoreGroup + 4 * (lane & 3);
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&s_out[i * kScoreGroup + 4 * (lane & 3)]);
+      float* dst = scores + (size_t)t * score_stride + c;
+      if (c + 3 < n_c) {
+        *reinterpret_cast<f32x4_t*>(dst) = v;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (c + k < n_c) dst[k] = v[k];
+      }
     }
   }
 }
@@ -169,7 +229,10 @@ hipError_t launch_index(const IndexArgs& a, hipStream_t stream) {
     // at most 16 waves per CU
     const int64_t groups_bound =
         (int64_t)nq * ((a.max_pos / kBlock + kScoreGroup - 1) / kScoreGroup);
-    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(groups_bound / 2, 4096));
+    // at most kWaveGroups groups per wave; at most 16 waves per CU otherwise
+    const int64_t want = std::min<int64_t>(groups_bound / 2, 4096);
+    const int grid = (int)std::max<int64_t>(
+        1, std::max<int64_t>(want, (groups_bound + kWaveGroups - 1) / kWaveGroups));
     hipLaunchKernelGGL(score_kernel, dim3(grid), dim3(64), 0, stream, nq,
                        a.idx_q + (size_t)q0 * kIdxHeads * kIdxDim, a.idx_w + (size_t)q0 * kIdxHeads,
                        a.q_req + q0, a.q_pos + q0, a.page_table, a.pt_stride, a.page_size, a.comp,
