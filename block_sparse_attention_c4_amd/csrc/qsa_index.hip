@@ -59,7 +59,8 @@ __global__ void __launch_bounds__(64)
 score_kernel(int nq, const uint16_t* __restrict__ idx_q, const float* __restrict__ idx_w,
              const int32_t* __restrict__ q_req, const int32_t* __restrict__ q_pos,
              const int32_t* __restrict__ page_table, int pt_stride, int page_size,
-             const uint16_t* __restrict__ comp, float* __restrict__ scores, int score_stride) {
+             const uint16_t* __restrict__ comp, float* __restrict__ scores, int score_stride,
+             float* __restrict__ gmax) {
   __shared__ float s_out[kWaveGroups * kScoreGroup];
   __shared__ int s_tg[kWaveGroups];    // query << 16 | group, per group of the range
   const int lane = threadIdx.x;
@@ -166,15 +167,22 @@ score_kernel(int nq, const uint16_t* __restrict__ idx_q, const float* __restrict
     compute(i + 1, kv1, q1);
   }
 
-  // write the range's scores: lane l covers group l / 4, blocks 4 (l % 4) .. +3
+  // write the range's scores and each group's maximum: lane l covers group l / 4,
+  // blocks 4 (l % 4) .. +3.  Past the last block the scores repeat the last block's
+  // (the loads were clamped), so the maximum is that of the visible blocks.
+  const int gstride = score_stride / kScoreGroup;
   for (int i0 = 0; i0 < ng; i0 += 16) {
     const int i = min(i0 + (lane >> 2), ng - 1);
     const int tg = s_tg[i];
     const int t = tg >> 16;
     const int n_c = __shfl(my_nc, t, 64);     // every lane active: its own query's count
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&s_out[i * kScoreGroup + 4 * (lane & 3)]);
+    float m = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+    m = fmaxf(m, dpp_f<0xb1>(m));            // quad_perm [1,0,3,2]
+    m = fmaxf(m, dpp_f<0x4e>(m));            // quad_perm [2,3,0,1]
     if (i0 + (lane >> 2) < ng) {
+      if ((lane & 3) == 0) gmax[(size_t)t * gstride + (tg & 0xffff)] = m;
       const int c = (tg & 0xffff) * kScoreGroup + 4 * (lane & 3);
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&s_out[i * kScoreGroup + 4 * (lane & 3)]);
       float* dst = scores + (size_t)t * score_stride + c;
       if (c + 3 < n_c) {
         *reinterpret_cast<f32x4_t*>(dst) = v;
@@ -189,13 +197,15 @@ score_kernel(int nq, const uint16_t* __restrict__ idx_q, const float* __restrict
 
 }  // namespace
 
-// Workspace: FP32 score rows [total_q, stride]; the code rows and group maxima of
-// the MFMA path live in the same bytes (the FP32 rows are written only after every
-// code has been read).  Then the queue of rows handed to the FP32 select.
+// Workspace: FP32 score rows [total_q, stride], then FP32 group maxima
+// [total_q, stride / 16] (decode scorer); the code rows and 16-bit group maxima of
+// the MFMA path live in the score rows' bytes (the FP32 rows are written only after
+// every code has been read).  Then the queue of rows handed to the FP32 select.
 static size_t score_rows_bytes(int total_q, int max_pos, int* stride) {
   const int nb = (max_pos + kBlock - 1) / kBlock;
   *stride = ((nb + 127) / 128) * 128;
-  return ((size_t)total_q * *stride * sizeof(float) + 255) / 256 * 256;
+  const size_t floats = (size_t)total_q * *stride + (size_t)total_q * (*stride / kScoreGroup);
+  return (floats * sizeof(float) + 255) / 256 * 256;
 }
 
 size_t index_workspace_bytes(int total_q, int max_pos) {
@@ -208,6 +218,7 @@ void index_workspace_carve(IndexArgs& a, void* ws) {
   const size_t rows = score_rows_bytes(a.total_q, a.max_pos, &a.score_stride);
   char* base = static_cast<char*>(ws);
   a.scores = reinterpret_cast<float*>(base);
+  a.gmax_f = a.scores + (size_t)a.total_q * a.score_stride;
   a.codes = reinterpret_cast<uint16_t*>(base);
   a.gmax = a.codes + (size_t)a.total_q * a.score_stride;
   a.queue = reinterpret_cast<int*>(base + rows);
@@ -236,7 +247,8 @@ hipError_t launch_index(const IndexArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(score_kernel, dim3(grid), dim3(64), 0, stream, nq,
                        a.idx_q + (size_t)q0 * kIdxHeads * kIdxDim, a.idx_w + (size_t)q0 * kIdxHeads,
                        a.q_req + q0, a.q_pos + q0, a.page_table, a.pt_stride, a.page_size, a.comp,
-                       a.scores + (size_t)q0 * a.score_stride, a.score_stride);
+                       a.scores + (size_t)q0 * a.score_stride, a.score_stride,
+                       a.gmax_f + (size_t)q0 * (a.score_stride / kScoreGroup));
   }
   launch_topk(a, stream);
   return hipGetLastError();

@@ -36,6 +36,7 @@ struct IndexArgs {
   int32_t* sel_count;
   // workspace
   float* scores;       // [total_q, score_stride] FP32 scores
+  float* gmax_f;       // [total_q, score_stride / 16] their 16-block group maxima
   uint16_t* codes;     // [total_q, score_stride] score codes (aliases scores)
   uint16_t* gmax;      // [total_q, score_stride / 16] group maxima of the codes (aliases scores)
   int* queue;          // [1 + total_q]: count, then rows handed to the FP32 select

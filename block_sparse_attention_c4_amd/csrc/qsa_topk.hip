@@ -14,7 +14,9 @@
 //  1. n <= 512: every block is kept.
 //  2. Lower bound: the 512th largest quad maximum t0 (found to 16 bits below the
 //     keys' common prefix, rounded down) has at least 512 quads, hence 512 scores,
-//     at or above it.  (Skipped when n <= 4096: t0 = 0.)
+//     at or above it.  (Skipped when n <= 4096: t0 = 0.)  Rows of more than 4096
+//     blocks use the scorer's 16-block group maxima instead and read only the
+//     groups whose maximum reaches the bound.
 //  3. Scores >= t0 go to LDS as candidates (a block-wide prefix count gives their
 //     slots); typically a thousand or fewer.
 //  4. Exact radix select over the candidates: the threshold key and how many keys
@@ -300,7 +302,70 @@ __device__ __forceinline__ void topk_quads(const float* srow, int n) {
   __syncthreads();
 }
 
+// Candidates from the scorer's 16-block group maxima (EG per thread): the 512th
+// largest maximum (found to a lower bound) has at least 512 groups, hence 512
+// scores, at or above it, so only the groups whose maximum reaches it are read.
+// Candidates take LDS slots (a wave prefix sum, one atomic per wave); misc[2] =
+// their count.
+template <int EG>
+__device__ __forceinline__ void topk_groups(const float* srow, const float* grow, int n) {
+  const int tid = threadIdx.x;
+  const int ng = (n + kScoreGroup - 1) / kScoreGroup;
+  uint32_t gk[EG];
+#pragma unroll
+  for (int e = 0; e < EG; ++e) {
+    const int g = tid + kT * e;
+    gk[e] = g < ng ? float_key(grow[g]) : 0u;
+  }
+  if (tid == 0) sm.misc[2] = 0;
+  const uint32_t t0 = max(select_keys<EG>(gk, kTopK, true).x, 1u);   // (its barriers order misc[2])
+  // one pass per e, wave-uniform: a lane reads its group only if it is a candidate;
+  // slots come from a wave prefix sum and one LDS atomic per wave
+  f32x4_t vals[EG][4];                 // every pass's loads are issued before any is used
+#pragma unroll
+  for (int e = 0; e < EG; ++e) {
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(srow + kScoreGroup * (tid + kT * e));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) vals[e][q] = gk[e] >= t0 ? src[q] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int e = 0; e < EG; ++e) {
+    const int g = tid + kT * e;
+    const bool cand = gk[e] >= t0;
+    uint32_t k[16];
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4_t v = vals[e][q];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = kScoreGroup * g + 4 * q + i;
+        const uint32_t key = float_key(v[i]);
+        k[4 * q + i] = (cand && c < n && key >= t0) ? key : 0u;
+        cnt += k[4 * q + i] ? 1 : 0;
+      }
+    }
+    const int incl = wave_inclusive_sum(cnt);
+    const int wtot = __builtin_amdgcn_readlane(incl, 63);
+    int base = 0;
+    if ((tid & 63) == 63 && wtot > 0) base = atomicAdd(&sm.misc[2], wtot);
+    base = __builtin_amdgcn_readlane(base, 63);
+    int slot = base + incl - cnt;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (k[i]) {
+        if (slot < kCap) {
+          sm.key[slot] = k[i];
+          sm.idx[slot] = (uint16_t)(kScoreGroup * g + i);
+        }
+        ++slot;
+      }
+  }
+  __syncthreads();
+}
+
 __device__ __forceinline__ void topk_row(int t, const float* __restrict__ scores, int score_stride,
+                                         const float* __restrict__ gmax,
                                          const int32_t* __restrict__ q_pos,
                                          int32_t* __restrict__ sel_blocks, int32_t* __restrict__ sel_pos,
                                          int sel_stride, int32_t* __restrict__ sel_count) {
@@ -332,7 +397,10 @@ __device__ __forceinline__ void topk_row(int t, const float* __restrict__ scores
 
   // candidates (scores >= a lower bound of the 512th) -> sm.key / sm.idx
   const int nq = (n + 3) / 4;
+  const float* grow = gmax ? gmax + (size_t)t * (score_stride / kScoreGroup) : nullptr;
   if (nq <= 4 * kT) topk_quads<4, true>(srow, n);
+  else if (grow && n <= 2 * kT * kScoreGroup) topk_groups<2>(srow, grow, n);
+  else if (grow) topk_groups<4>(srow, grow, n);
   else if (nq <= 8 * kT) topk_quads<8, true>(srow, n);
   else topk_quads<16, false>(srow, n);
 
@@ -434,10 +502,10 @@ __device__ __forceinline__ void topk_row(int t, const float* __restrict__ scores
 }
 
 __global__ void __launch_bounds__(kT)
-topk_kernel(const float* __restrict__ scores, int score_stride, const int32_t* __restrict__ q_pos,
-            int32_t* __restrict__ sel_blocks, int32_t* __restrict__ sel_pos, int sel_stride,
-            int32_t* __restrict__ sel_count) {
-  topk_row(blockIdx.x, scores, score_stride, q_pos, sel_blocks, sel_pos, sel_stride, sel_count);
+topk_kernel(const float* __restrict__ scores, int score_stride, const float* __restrict__ gmax,
+            const int32_t* __restrict__ q_pos, int32_t* __restrict__ sel_blocks,
+            int32_t* __restrict__ sel_pos, int sel_stride, int32_t* __restrict__ sel_count) {
+  topk_row(blockIdx.x, scores, score_stride, gmax, q_pos, sel_blocks, sel_pos, sel_stride, sel_count);
 }
 
 // The rows listed in queue[1 .. queue[0]] (rows the code-based select hands over).
@@ -449,7 +517,8 @@ topk_queued_kernel(const int* __restrict__ queue, const float* __restrict__ scor
   const int nq = queue[0];
   for (int k = blockIdx.x; k < nq; k += gridDim.x) {
     __syncthreads();                   // LDS of the previous row is free
-    topk_row(queue[1 + k], scores, score_stride, q_pos, sel_blocks, sel_pos, sel_stride, sel_count);
+    topk_row(queue[1 + k], scores, score_stride, nullptr, q_pos, sel_blocks, sel_pos, sel_stride,
+             sel_count);
   }
 }
 
@@ -457,7 +526,7 @@ topk_queued_kernel(const int* __restrict__ queue, const float* __restrict__ scor
 
 void launch_topk(const IndexArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(topk_kernel, dim3(a.total_q), dim3(kT), 0, stream, a.scores, a.score_stride,
-                     a.q_pos, a.sel_blocks, a.sel_pos, a.sel_stride, a.sel_count);
+                     a.gmax_f, a.q_pos, a.sel_blocks, a.sel_pos, a.sel_stride, a.sel_count);
 }
 
 void launch_topk_queued(const IndexArgs& a, hipStream_t stream) {
