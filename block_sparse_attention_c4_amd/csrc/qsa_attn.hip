@@ -274,6 +274,9 @@ attn_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ q_req,
 }
 
 // Merge the split partials of one (query, KV head): 256 threads, thread = (head, 8 dims).
+// Every split's partial is requested before any is used (one memory round trip).
+constexpr int kMaxCombine = 8;         // splits merged from registers; more loop over memory
+
 __global__ void __launch_bounds__(256)
 combine_kernel(const float* __restrict__ part, int splits, uint16_t* __restrict__ out,
                float* __restrict__ lse) {
@@ -284,27 +287,45 @@ combine_kernel(const float* __restrict__ part, int splits, uint16_t* __restrict_
   const int h = tid >> 5;
   const int d0 = (tid & 31) * 8;
   const float* base = part + (size_t)tg * splits * kPartFloats;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) {
-    const float* pp = base + (size_t)s * kPartFloats;
-    M = fmaxf(M, pp[kGroup + h] > 0.f ? pp[h] : -INFINITY);
-  }
-  float L = 0.f;
+  float M = -INFINITY, L = 0.f;
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < splits; ++s) {
-    const float* pp = base + (size_t)s * kPartFloats;
-    const float ls = pp[kGroup + h];
-    const float* pa = pp + 2 * kGroup + h * kHeadDim + d0;
-    const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(pa);
-    const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(pa + 4);
-    // an empty split wrote l = 0 and zero accumulators: its weight is 0
-    const float sc = (ls > 0.f) ? exp2f(pp[h] - M) : 0.f;
-    L += sc * ls;
+  for (int s0 = 0; s0 < splits; s0 += kMaxCombine) {
+    const int ns = min(kMaxCombine, splits - s0);
+    float ms[kMaxCombine], ls[kMaxCombine];
+    f32x4_t a0[kMaxCombine], a1[kMaxCombine];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      o[e] += sc * a0[e];
-      o[4 + e] += sc * a1[e];
+    for (int i = 0; i < kMaxCombine; ++i) {
+      if (i < ns) {
+        const float* pp = base + (size_t)(s0 + i) * kPartFloats;
+        ms[i] = pp[h];
+        ls[i] = pp[kGroup + h];
+        a0[i] = *reinterpret_cast<const f32x4_t*>(pp + 2 * kGroup + h * kHeadDim + d0);
+        a1[i] = *reinterpret_cast<const f32x4_t*>(pp + 2 * kGroup + h * kHeadDim + d0 + 4);
+      }
     }
+    // an empty split wrote l = 0 and zero accumulators: its weight is 0
+    float Mn = M;
+#pragma unroll
+    for (int i = 0; i < kMaxCombine; ++i)
+      if (i < ns && ls[i] > 0.f) Mn = fmaxf(Mn, ms[i]);
+    if (Mn == -INFINITY) continue;
+    const float rescale = M == -INFINITY ? 0.f : exp2f(M - Mn);
+    L *= rescale;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= rescale;
+#pragma unroll
+    for (int i = 0; i < kMaxCombine; ++i) {
+      if (i < ns && ls[i] > 0.f) {
+        const float sc = exp2f(ms[i] - Mn);
+        L += sc * ls[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[e] += sc * a0[i][e];
+          o[4 + e] += sc * a1[i][e];
+        }
+      }
+    }
+    M = Mn;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint16_t* orow = out + ((size_t)t * kQHeads + g * kGroup + h) * kHeadDim + d0;
