@@ -313,11 +313,14 @@ score_mfma_kernel(int total_q, const uint16_t* __restrict__ idx_q, const float* 
 
 constexpr int kTT = 256;               // threads per row
 constexpr int kTW = kTT / 64;
-constexpr int kEnt = 32;               // entries per thread
-constexpr int kListCap = kTT * kEnt;   // 8192 candidates
+constexpr int kEnt = 32;               // entries per thread (register-held)
+constexpr int kRowCap = kTT * kEnt;    // rows of at most 8192 blocks are read whole
+constexpr int kListCap = 2048;         // LDS candidates of the longer rows
+static_assert(kListCap % kTT == 0 && kListCap <= kRowCap, "list entries map onto the register entries");
 constexpr int kTieCap = 1024;          // blocks sharing the threshold code
 constexpr int kWords = kMaxBlocks / 32;
 constexpr int kWordsPerThread = kWords / kTT;   // 8
+constexpr int kCandPass = 3;          // candidate groups per thread per load pass
 
 struct __attribute__((aligned(16))) SmemC {
   uint32_t red[2 * kTW];
@@ -454,8 +457,6 @@ topk_codes_kernel(const uint16_t* __restrict__ codes, const uint16_t* __restrict
   const uint16_t* crow = codes + (size_t)t * stride;
   const int nwords = (n + 31) / 32;
   const int w0 = kWordsPerThread * tid;
-#pragma unroll
-  for (int i = 0; i < kWordsPerThread; ++i) sc.bits[w0 + i] = 0u;
   if (tid == 0) {
     sc.misc[4] = 0;                    // list length
     sc.misc[5] = 0;                    // tie count
@@ -465,7 +466,7 @@ topk_codes_kernel(const uint16_t* __restrict__ codes, const uint16_t* __restrict
   // whose maximum reaches the 512th largest group maximum (at least 512 blocks of
   // the row reach that value, so the 512 best are among them)
   uint32_t ent[kEnt];
-  if (n <= kListCap) {
+  if (n <= kRowCap) {
 #pragma unroll
     for (int e = 0; e < kEnt / 8; ++e) {
       const int ch = tid + kTT * e;
@@ -490,32 +491,61 @@ topk_codes_kernel(const uint16_t* __restrict__ codes, const uint16_t* __restrict
         gk[8 * e + i] = 8 * ch + i < ng ? (v[i / 2] >> (16 * (i & 1))) & 0xffffu : 0u;
     }
     const uint32_t gstar = (uint32_t)select16<16>(gk, kTopK).x;
+    // compact the candidate groups (maximum >= gstar) into the bitmap words, which
+    // are cleared only after the list is built
+    uint16_t* cand = reinterpret_cast<uint16_t*>(sc.bits);   // room for kWords * 2 >= 4096
+    int nmine = 0;
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
+    for (int j = 0; j < 16; ++j) nmine += gk[j] >= gstar ? 1 : 0;   // gk = 0 is never >= gstar > 0
+    const int2 cs = block_scan256(nmine);
+    {
+      int slot = cs.x;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (gk[8 * e + i] < gstar) continue;
-        const int g = 8 * (tid + kTT * e) + i;
-        const u32x4_t a = ld16(crow + kScoreGroup * g);
-        const u32x4_t b = ld16(crow + kScoreGroup * g + 8);
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (gk[8 * e + i] >= gstar) cand[slot++] = (uint16_t)(8 * (tid + kTT * e) + i);
+    }
+    __syncthreads();
+    const int ncand = cs.y;
+    // every candidate's codes are requested before any is used: kCandPass groups per
+    // thread per pass; list slots come from a wave prefix count and one atomic per wave
+    for (int j0 = 0; j0 < ncand; j0 += kCandPass * kTT) {
+      u32x4_t a[kCandPass], b[kCandPass];
+      int gg[kCandPass];
+#pragma unroll
+      for (int r = 0; r < kCandPass; ++r) {
+        const int j = j0 + kTT * r + tid;
+        gg[r] = j < ncand ? (int)cand[j] : -1;
+        const uint16_t* src = crow + kScoreGroup * max(gg[r], 0);
+        a[r] = gg[r] >= 0 ? ld16(src) : u32x4_t{0u, 0u, 0u, 0u};
+        b[r] = gg[r] >= 0 ? ld16(src + 8) : u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int r = 0; r < kCandPass; ++r) {
         uint32_t keep[16];
         int k = 0;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const uint32_t word = j < 8 ? a[j / 2] : b[(j - 8) / 2];
-          const uint32_t code = (word >> (16 * (j & 1))) & 0xffffu;
-          const int c = kScoreGroup * g + j;
-          keep[j] = (c < n && code >= gstar) ? (code << 16) | (uint32_t)c : 0u;
-          k += keep[j] ? 1 : 0;
+        for (int jj = 0; jj < 16; ++jj) {
+          const uint32_t word = jj < 8 ? a[r][jj / 2] : b[r][(jj - 8) / 2];
+          const uint32_t code = (word >> (16 * (jj & 1))) & 0xffffu;
+          const int c = kScoreGroup * gg[r] + jj;
+          keep[jj] = (gg[r] >= 0 && c < n && code >= gstar) ? (code << 16) | (uint32_t)c : 0u;
+          k += keep[jj] ? 1 : 0;
         }
-        int slot = atomicAdd(&sc.misc[4], k);
+        const int incl = wave_inclusive_sum(k);
+        const int wtot = __builtin_amdgcn_readlane(incl, 63);
+        int base = 0;
+        if ((tid & 63) == 63 && wtot > 0) base = atomicAdd(&sc.misc[4], wtot);
+        int slot = __builtin_amdgcn_readlane(base, 63) + incl - k;
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (keep[j]) {
-            if (slot < kListCap) sc.list[slot] = keep[j];
+        for (int jj = 0; jj < 16; ++jj)
+          if (keep[jj]) {
+            if (slot < kListCap) sc.list[slot] = keep[jj];
             ++slot;
           }
       }
+    }
     __syncthreads();
     const int len = sc.misc[4];
     if (len > kListCap) {              // heavy ties: the FP32 path takes the row
@@ -525,9 +555,12 @@ topk_codes_kernel(const uint16_t* __restrict__ codes, const uint16_t* __restrict
 #pragma unroll
     for (int e = 0; e < kEnt; ++e) {
       const int i = tid + kTT * e;
-      ent[e] = i < len ? sc.list[i] : 0u;
+      ent[e] = (e < kListCap / kTT && i < len) ? sc.list[i] : 0u;
     }
   }
+  // the bitmap (the candidate groups' scratch above) starts empty
+#pragma unroll
+  for (int i = 0; i < kWordsPerThread; ++i) sc.bits[w0 + i] = 0u;
 
   // ---- the 512th largest code T: codes above it are kept; of the cnt entries equal
   // to T, `need` are kept, ranked by exact score
