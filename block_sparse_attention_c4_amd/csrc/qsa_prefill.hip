@@ -548,7 +548,9 @@ topk_codes_kernel(const uint16_t* __restrict__ codes, const uint16_t* __restrict
     }
     __syncthreads();
     const int len = sc.misc[4];
-    if (len > kListCap) {              // heavy ties: the FP32 path takes the row
+    // heavy ties (more candidates than the list holds), or fewer than 512 candidates
+    // (maxima that do not match the codes): the FP32 path takes the row
+    if (len > kListCap || len < kTopK) {
       queue_row(queue, t);
       return;
     }
@@ -583,7 +585,10 @@ topk_codes_kernel(const uint16_t* __restrict__ codes, const uint16_t* __restrict
   }
   __syncthreads();
   if (need != cnt) {
-    if (cnt > kTieCap) {
+    // the tied entries written above number cnt whenever the codes and maxima come
+    // from one scorer pass; otherwise (or beyond the tie buffer) the FP32 path takes
+    // the row
+    if (cnt > kTieCap || sc.misc[5] != cnt) {
       queue_row(queue, t);
       return;
     }
@@ -598,7 +603,7 @@ topk_codes_kernel(const uint16_t* __restrict__ codes, const uint16_t* __restrict
     for (int h = 0; h < kIdxHeads; ++h) wq[h] = idx_w[(size_t)t * kIdxHeads + h];
     for (int j0 = 16 * w; j0 < cnt; j0 += 16 * kTW) {
       const int j = j0 + (lane & 15);
-      const int c = sc.tie_idx[min(j, cnt - 1)];
+      const int c = min((int)sc.tie_idx[min(j, cnt - 1)], n - 1);
       const float s = score16(af, comp + comp_row(pt_row, c, bpp) * kIdxDim, wq);
       if (lane < 16 && j < cnt) sc.tie_key[j] = float_key(s);
     }
