@@ -10,7 +10,7 @@
 //
 // With thousands of queries on the same keys the scores are a dense contraction:
 // [T*4 query-head rows x 128] x [128 x blocks].  score_mfma_kernel computes it with
-// v_mfma_f32_16x16x32_bf16, one 64-query x 1024-block tile per work group.  The A
+// v_mfma_f32_16x16x32_bf16, one 64-query x 2048-block tile per work group.  The A
 // operand holds 4 queries x 4 heads per 16 rows, so each lane of the result holds
 // the 4 head dots of one (query, block) pair and mixes them in registers.
 //
@@ -32,7 +32,7 @@ namespace qsa {
 namespace {
 
 constexpr int kPfQ = 64;         // queries per scorer work group (4 waves x 16)
-constexpr int kPfRange = 1024;   // blocks per scorer work group
+constexpr int kPfRange = 2048;   // blocks per scorer work group
 constexpr int kLdsRow = 136;     // bf16 per staged key row: 128 + 8 to spread LDS banks
 
 __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
@@ -89,7 +89,7 @@ __device__ __forceinline__ float score16(const u32x4_t (&af)[4], const uint16_t*
 
 // ------------------------------------------------------------------ scorer
 
-// A work group is 4 waves over a 64-query x 1024-block tile; a wave owns 16 queries
+// A work group is 4 waves over a 64-query x 2048-block tile; a wave owns 16 queries
 // (4 A tiles of 4 queries x 4 heads).  The block range is walked in phases of
 // kPhase groups of 16 blocks.  One phase: its keys (loaded into registers during
 // the previous phase) go to LDS; the next phase's keys are requested; the previous
@@ -103,7 +103,8 @@ constexpr int kATiles = kPfQ / (4 * kSW);            // A tiles per wave: 4
 constexpr int kQW = 4 * kATiles;                     // queries per wave
 constexpr int kPhase = 8;
 constexpr int kStage = kPhase * 256 / kST;           // 16-byte key chunks per thread per phase
-constexpr int kCodeRow = kPhase * kScoreGroup + 8;   // u16 per staged code row (+8 spreads banks)
+constexpr int kCodeRow = kPhase * kScoreGroup + 16;  // u16 per staged code row (+16: the 4 query rows of
+                                                     // an epilogue store fall in distinct banks)
 static_assert(kPhase % 4 == 0 && kST >= 4 * kPfQ, "the flush covers 64 queries x kPhase groups");
 
 __global__ void __launch_bounds__(kST, 2)
