@@ -53,6 +53,14 @@ SMALL = {
         hot_per_req=6),
     "indexshare_small": lambda: synth.make_workload(
         "indexshare_small", "indexshare", 304, [4100, 33003, 700], reuse_steps=3),
+    # more than 64 decode queries: the scorer launches in chunks of 64 queries
+    "decode_batch70": lambda: synth.make_workload(
+        "decode_batch70", "decode", 305,
+        [3, 700, 2051, 40000] + [1 + (i * 7919) % 20000 for i in range(66)], hot_per_req=2),
+    # a prefill chunk of fewer than 64 queries: the paged-GEMV scorer and the FP32
+    # select, with 20 queries per request
+    "prefill_small_chunk": lambda: synth.make_workload(
+        "prefill_small_chunk", "prefill", 306, [5000, 40000], chunk=20),
 }
 
 
