@@ -39,6 +39,7 @@ constexpr int kT = 1024;               // threads per work group
 constexpr int kW = kT / 64;
 constexpr int kCap = 4096;             // LDS candidates
 constexpr int kWords = kMaxBlocks / 32;   // 2048 bitmap words, 2 per thread
+constexpr int kRankCap = 256;          // keys ranked directly after the first select pass
 
 struct __attribute__((aligned(16))) Smem {
   uint32_t red[2 * kW];
@@ -49,7 +50,8 @@ struct __attribute__((aligned(16))) Smem {
   uint32_t bits[kWords];
   uint32_t eqbits[kWords];
   uint16_t wpre[kWords];               // kept bits in the words before each word
-  int misc[4];
+  uint32_t rank_key[kRankCap];
+  int misc[8];
 };
 
 __shared__ Smem sm;
@@ -139,6 +141,7 @@ __device__ __forceinline__ uint2 select_keys(const uint32_t (&key)[E], int kk, b
     sm.red[kW + w] = mn;
   }
   if (tid < 256) sm.hist[0][tid] = 0u;
+  if (tid == 0) sm.misc[4] = 0;        // keys gathered for ranking
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < kW / 4; ++i) {
@@ -170,6 +173,33 @@ __device__ __forceinline__ uint2 select_keys(const uint32_t (&key)[E], int kk, b
     if (bin > 0) lo_key = max(mn, float_key(fmn + (float)(bin - 1) / scale));
     if (bin < 255) hi_key = min(mx, float_key(fmn + (float)(bin + 2) / scale));
     if (lower_bound) return make_uint2(lo_key, 0u);
+    // Few keys in the chosen bin (the usual case): gather them and rank each against
+    // the others, instead of radix passes with two barriers each.
+    const int m = (int)sm.hist[0][bin];
+    if (m <= kRankCap) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const uint32_t k = key[e];
+        if (k != 0u && min(255, (int)((key_float(k) - fmn) * scale)) == bin)
+          sm.rank_key[atomicAdd(&sm.misc[4], 1)] = k;
+      }
+      __syncthreads();
+      for (int i = tid; i < m; i += kT) {
+        const uint32_t ki = sm.rank_key[i];
+        int gt = 0, ge = 0;
+        for (int j = 0; j < m; ++j) {
+          const uint32_t kj = sm.rank_key[j];
+          gt += kj > ki ? 1 : 0;
+          ge += kj >= ki ? 1 : 0;
+        }
+        if (gt < kk && kk <= ge) {     // ki is the kk-th largest of the bin
+          sm.misc[5] = (int)ki;
+          sm.misc[6] = kk - gt;
+        }
+      }
+      __syncthreads();
+      return make_uint2((uint32_t)sm.misc[5], (uint32_t)sm.misc[6]);
+    }
   }
   // radix passes over r = key - lo_key among the keys in play
   const uint32_t range = hi_key - lo_key;
