@@ -316,9 +316,9 @@ constexpr int kTT = 256;               // threads per row
 constexpr int kTW = kTT / 64;
 constexpr int kEnt = 32;               // entries per thread (register-held)
 constexpr int kRowCap = kTT * kEnt;    // rows of at most 8192 blocks are read whole
-constexpr int kListCap = 2048;         // LDS candidates of the longer rows
+constexpr int kListCap = 1024;         // LDS candidates of the longer rows (about 600 typical)
 static_assert(kListCap % kTT == 0 && kListCap <= kRowCap, "list entries map onto the register entries");
-constexpr int kTieCap = 1024;          // blocks sharing the threshold code
+constexpr int kTieCap = 256;           // blocks sharing the threshold code (a few dozen typical)
 constexpr int kWords = kMaxBlocks / 32;
 constexpr int kWordsPerThread = kWords / kTT;   // 8
 constexpr int kCandPass = 3;          // candidate groups per thread per load pass
@@ -376,18 +376,20 @@ __device__ __forceinline__ void find_bin(int buf, int kk) {
   }
 }
 
-// kk-th largest 16-bit value among the non-zero v[] of the work group.  Returns
-// (value T, how many entries equal to T are kept, how many entries equal T).
-template <int E>
+// kk-th largest 16-bit value among the non-zero values (v[] >> kShift) of the work
+// group.  Returns (value T, how many entries equal to T are kept, how many entries
+// equal T).  kShift = 16 reads the codes of packed (code << 16 | block) entries.
+template <int E, int kShift = 0>
 __device__ __forceinline__ int3 select16(const uint32_t (&v)[E], int kk) {
   const int tid = threadIdx.x, w = tid >> 6;
   uint32_t mx = 0u, mn = 0xffffu;
   int cnt = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    mx = max(mx, v[e]);
-    mn = min(mn, v[e] ? v[e] : 0xffffu);
-    cnt += v[e] ? 1 : 0;
+    const uint32_t x = v[e] >> kShift;
+    mx = max(mx, x);
+    mn = min(mn, x ? x : 0xffffu);
+    cnt += x ? 1 : 0;
   }
   mx = wave_max_u32(mx);
   mn = wave_min_u32(mn);
@@ -412,8 +414,10 @@ __device__ __forceinline__ int3 select16(const uint32_t (&v)[E], int kk) {
     const uint32_t pmask = ~((2u << hi) - 1u);
     const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (v[e] && (v[e] & pmask) == prefix) atomicAdd(&sc.hist[buf][(v[e] >> lo) & dmask], 1u);
+    for (int e = 0; e < E; ++e) {
+      const uint32_t x = v[e] >> kShift;
+      if (x && (x & pmask) == prefix) atomicAdd(&sc.hist[buf][(x >> lo) & dmask], 1u);
+    }
     __syncthreads();
     find_bin(buf, kk);
     __syncthreads();
@@ -432,7 +436,7 @@ __device__ __forceinline__ void queue_row(int* queue, int t) {
   if (threadIdx.x == 0) queue[1 + atomicAdd(queue, 1)] = t;
 }
 
-__global__ void __launch_bounds__(kTT)
+__global__ void __launch_bounds__(kTT, 6)   // six rows per CU (16 KB of LDS, <= 80 VGPRs each)
 topk_codes_kernel(const uint16_t* __restrict__ codes, const uint16_t* __restrict__ gmax, int stride,
                   const int32_t* __restrict__ q_req, const int32_t* __restrict__ q_pos,
                   const uint16_t* __restrict__ idx_q, const float* __restrict__ idx_w,
@@ -463,11 +467,104 @@ topk_codes_kernel(const uint16_t* __restrict__ codes, const uint16_t* __restrict
     sc.misc[5] = 0;                    // tie count
   }
 
+  // ---- from the entries (code << 16 | block) of this thread, E per thread: the
+  // threshold, the kept blocks and the expanded output
+  auto finish = [&](auto& ent) {
+    constexpr int E = (int)(sizeof(ent) / sizeof(ent[0]));
+    // the bitmap (the candidate groups' scratch above) starts empty
+#pragma unroll
+    for (int i = 0; i < kWordsPerThread; ++i) sc.bits[w0 + i] = 0u;
+
+    // ---- the 512th largest code T: codes above it are kept; of the cnt entries equal
+    // to T, `need` are kept, ranked by exact score
+    const int3 sel = select16<E, 16>(ent, kTopK);
+    const uint32_t T = (uint32_t)sel.x;
+    const int need = sel.y, cnt = sel.z;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint32_t cve = ent[e] >> 16;
+      if (!ent[e] || cve < T) continue;
+      const int c = (int)(ent[e] & 0xffffu);
+      if (cve > T || need == cnt) {
+        mark(c);
+      } else {
+        const int slot = atomicAdd(&sc.misc[5], 1);
+        if (slot < kTieCap) sc.tie_idx[slot] = (uint16_t)c;
+      }
+    }
+    __syncthreads();
+    if (need != cnt) {
+      // the tied entries written above number cnt whenever the codes and maxima come
+      // from one scorer pass; otherwise (or beyond the tie buffer) the FP32 path takes
+      // the row
+      if (cnt > kTieCap || sc.misc[5] != cnt) {
+        queue_row(queue, t);
+        return;
+      }
+      // exact scores of the tied blocks (same MFMA arithmetic as the scorer)
+      const int lane = tid & 63, w = tid >> 6;
+      const int bpp = page_size / kBlock;
+      const int32_t* pt_row = page_table + (size_t)q_req[t] * pt_stride;
+      u32x4_t af[4];
+      query_rows(idx_q, t, af);
+      float wq[kIdxHeads];
+#pragma unroll
+      for (int h = 0; h < kIdxHeads; ++h) wq[h] = idx_w[(size_t)t * kIdxHeads + h];
+      for (int j0 = 16 * w; j0 < cnt; j0 += 16 * kTW) {
+        const int j = j0 + (lane & 15);
+        const int c = min((int)sc.tie_idx[min(j, cnt - 1)], n - 1);
+        const float s = score16(af, comp + comp_row(pt_row, c, bpp) * kIdxDim, wq);
+        if (lane < 16 && j < cnt) sc.tie_key[j] = float_key(s);
+      }
+      __syncthreads();
+      // rank: higher score first, then lower block index
+      for (int j = tid; j < cnt; j += kTT) {
+        const uint32_t kj = sc.tie_key[j];
+        const int ij = sc.tie_idx[j];
+        int rank = 0;
+        for (int i = 0; i < cnt; ++i) {
+          const uint32_t ki = sc.tie_key[i];
+          rank += (ki > kj || (ki == kj && sc.tie_idx[i] < ij)) ? 1 : 0;
+        }
+        if (rank < need) mark(ij);
+      }
+      __syncthreads();
+    }
+
+    // ---- emit the kept blocks in index order, each expanded to its 4 positions
+    {
+      uint32_t wv[kWordsPerThread];
+      int k = 0;
+#pragma unroll
+      for (int i = 0; i < kWordsPerThread; ++i) {
+        wv[i] = w0 + i < nwords ? sc.bits[w0 + i] : 0u;
+        k += __popc(wv[i]);
+      }
+      int idx = block_scan256(k).x;
+#pragma unroll
+      for (int i = 0; i < kWordsPerThread; ++i)
+        for (uint32_t e = wv[i]; e; e &= e - 1) {
+          const int c = 32 * (w0 + i) + __ffs(e) - 1;
+          if (idx < kTopK) {             // exactly kTopK bits are set; the guard bounds the row
+            row_b[idx] = c;
+            *reinterpret_cast<int4*>(row_p + kBlock * idx) = make_int4(4 * c, 4 * c + 1, 4 * c + 2, 4 * c + 3);
+          }
+          ++idx;
+        }
+    }
+    const int base = kBlock * kTopK;
+    for (int i = base + tid; i < sel_stride; i += kTT) {
+      const int k = i - base;
+      row_p[i] = k < pend ? kBlock * n + k : -1;
+    }
+    if (tid == 0) sel_count[t] = base + pend;
+  };
+
   // ---- entries (code << 16 | block): the whole row, or the blocks of the groups
   // whose maximum reaches the 512th largest group maximum (at least 512 blocks of
   // the row reach that value, so the 512 best are among them)
-  uint32_t ent[kEnt];
   if (n <= kRowCap) {
+    uint32_t ent[kEnt];
 #pragma unroll
     for (int e = 0; e < kEnt / 8; ++e) {
       const int ch = tid + kTT * e;
@@ -479,6 +576,7 @@ topk_codes_kernel(const uint16_t* __restrict__ codes, const uint16_t* __restrict
         ent[8 * e + i] = c < n ? (code << 16) | (uint32_t)c : 0u;
       }
     }
+    finish(ent);
   } else {
     const int ng = (n + kScoreGroup - 1) / kScoreGroup;   // <= 4096
     const uint16_t* grow = gmax + (size_t)t * (stride / kScoreGroup);
@@ -555,101 +653,14 @@ topk_codes_kernel(const uint16_t* __restrict__ codes, const uint16_t* __restrict
       queue_row(queue, t);
       return;
     }
+    uint32_t ent[kListCap / kTT];
 #pragma unroll
-    for (int e = 0; e < kEnt; ++e) {
+    for (int e = 0; e < kListCap / kTT; ++e) {
       const int i = tid + kTT * e;
-      ent[e] = (e < kListCap / kTT && i < len) ? sc.list[i] : 0u;
+      ent[e] = i < len ? sc.list[i] : 0u;
     }
+    finish(ent);
   }
-  // the bitmap (the candidate groups' scratch above) starts empty
-#pragma unroll
-  for (int i = 0; i < kWordsPerThread; ++i) sc.bits[w0 + i] = 0u;
-
-  // ---- the 512th largest code T: codes above it are kept; of the cnt entries equal
-  // to T, `need` are kept, ranked by exact score
-  uint32_t cv[kEnt];
-#pragma unroll
-  for (int e = 0; e < kEnt; ++e) cv[e] = ent[e] >> 16;
-  const int3 sel = select16<kEnt>(cv, kTopK);
-  const uint32_t T = (uint32_t)sel.x;
-  const int need = sel.y, cnt = sel.z;
-#pragma unroll
-  for (int e = 0; e < kEnt; ++e) {
-    if (!ent[e] || cv[e] < T) continue;
-    const int c = (int)(ent[e] & 0xffffu);
-    if (cv[e] > T || need == cnt) {
-      mark(c);
-    } else {
-      const int slot = atomicAdd(&sc.misc[5], 1);
-      if (slot < kTieCap) sc.tie_idx[slot] = (uint16_t)c;
-    }
-  }
-  __syncthreads();
-  if (need != cnt) {
-    // the tied entries written above number cnt whenever the codes and maxima come
-    // from one scorer pass; otherwise (or beyond the tie buffer) the FP32 path takes
-    // the row
-    if (cnt > kTieCap || sc.misc[5] != cnt) {
-      queue_row(queue, t);
-      return;
-    }
-    // exact scores of the tied blocks (same MFMA arithmetic as the scorer)
-    const int lane = tid & 63, w = tid >> 6;
-    const int bpp = page_size / kBlock;
-    const int32_t* pt_row = page_table + (size_t)q_req[t] * pt_stride;
-    u32x4_t af[4];
-    query_rows(idx_q, t, af);
-    float wq[kIdxHeads];
-#pragma unroll
-    for (int h = 0; h < kIdxHeads; ++h) wq[h] = idx_w[(size_t)t * kIdxHeads + h];
-    for (int j0 = 16 * w; j0 < cnt; j0 += 16 * kTW) {
-      const int j = j0 + (lane & 15);
-      const int c = min((int)sc.tie_idx[min(j, cnt - 1)], n - 1);
-      const float s = score16(af, comp + comp_row(pt_row, c, bpp) * kIdxDim, wq);
-      if (lane < 16 && j < cnt) sc.tie_key[j] = float_key(s);
-    }
-    __syncthreads();
-    // rank: higher score first, then lower block index
-    for (int j = tid; j < cnt; j += kTT) {
-      const uint32_t kj = sc.tie_key[j];
-      const int ij = sc.tie_idx[j];
-      int rank = 0;
-      for (int i = 0; i < cnt; ++i) {
-        const uint32_t ki = sc.tie_key[i];
-        rank += (ki > kj || (ki == kj && sc.tie_idx[i] < ij)) ? 1 : 0;
-      }
-      if (rank < need) mark(ij);
-    }
-    __syncthreads();
-  }
-
-  // ---- emit the kept blocks in index order, each expanded to its 4 positions
-  {
-    uint32_t wv[kWordsPerThread];
-    int k = 0;
-#pragma unroll
-    for (int i = 0; i < kWordsPerThread; ++i) {
-      wv[i] = w0 + i < nwords ? sc.bits[w0 + i] : 0u;
-      k += __popc(wv[i]);
-    }
-    int idx = block_scan256(k).x;
-#pragma unroll
-    for (int i = 0; i < kWordsPerThread; ++i)
-      for (uint32_t e = wv[i]; e; e &= e - 1) {
-        const int c = 32 * (w0 + i) + __ffs(e) - 1;
-        if (idx < kTopK) {             // exactly kTopK bits are set; the guard bounds the row
-          row_b[idx] = c;
-          *reinterpret_cast<int4*>(row_p + kBlock * idx) = make_int4(4 * c, 4 * c + 1, 4 * c + 2, 4 * c + 3);
-        }
-        ++idx;
-      }
-  }
-  const int base = kBlock * kTopK;
-  for (int i = base + tid; i < sel_stride; i += kTT) {
-    const int k = i - base;
-    row_p[i] = k < pend ? kBlock * n + k : -1;
-  }
-  if (tid == 0) sel_count[t] = base + pend;
 }
 
 // Exact FP32 scores of the queued rows (into the FP32 score rows of the workspace,
