@@ -317,7 +317,7 @@ constexpr int kTW = kTT / 64;
 constexpr int kEnt = 32;               // entries per thread (register-held)
 constexpr int kRowCap = kTT * kEnt;    // rows of at most 8192 blocks are read whole
 constexpr int kListCap = 1024;         // LDS candidates of the longer rows (about 600 typical)
-static_assert(kListCap % kTT == 0 && kListCap <= kRowCap, "list entries map onto the register entries");
+static_assert(kListCap % kTT == 0, "the list is read back as kListCap / kTT entries per thread");
 constexpr int kTieCap = 256;           // blocks sharing the threshold code (a few dozen typical)
 constexpr int kWords = kMaxBlocks / 32;
 constexpr int kWordsPerThread = kWords / kTT;   // 8
