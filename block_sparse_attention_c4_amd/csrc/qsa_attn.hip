@@ -145,6 +145,7 @@ __device__ __forceinline__ void attend_step(SoftmaxState& st, const KV& x, const
 }
 
 constexpr int kMaxSplitLen = 2176;   // >= kMaxSel + QSA_MAX_EXTRA, a multiple of 128
+constexpr int kSlotsPer = (kMaxSplitLen + kThreads - 1) / kThreads;   // list entries per thread
 
 __global__ void __launch_bounds__(kThreads)
 attn_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ q_req,
@@ -152,7 +153,7 @@ attn_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ q_req,
             const int32_t* __restrict__ page_table, int pt_stride, int page_size,
             const int32_t* __restrict__ sel_pos, const int32_t* __restrict__ sel_count,
             int sel_stride, const int32_t* __restrict__ extra_pos, int n_extra, float scale_log2,
-            int splits, int split_len, float* __restrict__ part, uint16_t* __restrict__ out,
+            int splits, float* __restrict__ part, uint16_t* __restrict__ out,
             float* __restrict__ lse) {
   __shared__ float s_m[kWaves][kGroup];
   __shared__ float s_l[kWaves][kGroup];
@@ -178,20 +179,42 @@ attn_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ q_req,
     for (int k = 0; k < 8; ++k) qf[k] = (r < kGroup) ? ld16(qrow + 32 * k) : u32x4_t{0u, 0u, 0u, 0u};
   }
 
-  // translate this split's positions to pool slots once (-1 = no position)
+  // This split's share of the position list: the list's bound (2051 + extras)
+  // in 32-position chunks, dealt out evenly, so that every work group streams
+  // about the same bytes.
+  const int bound = kMaxSel + n_extra;
+  const int nchunk = (bound + kChunk - 1) / kChunk;
+  const int start = (sp * nchunk / splits) * kChunk;
+  const int span = min(((sp + 1) * nchunk / splits) * kChunk, bound) - start;
   const int req = q_req ? q_req[t] : t;
   const int cnt = sel_count[t];
   const int total = cnt + n_extra;
-  const int start = sp * split_len;
-  const int len = max(0, min(split_len, total - start));
+  const int len = max(0, min(span, total - start));
+  // Translate the positions to pool slots (-1 = no position).  All list loads
+  // go out before the count is needed, and all page-table loads go out
+  // together, so the translation costs two memory round trips.
   {
     const int32_t* pt_row = page_table + (size_t)req * pt_stride;
     const int32_t* lst = sel_pos + (size_t)t * sel_stride;
-    const int32_t* ext = extra_pos ? extra_pos + (size_t)t * n_extra : nullptr;
-    for (int i = tid; i < len; i += kThreads) {
-      const int li = start + i;
-      const int p = li < cnt ? lst[li] : ext[li - cnt];
-      s_slot[i] = p >= 0 ? (int32_t)token_slot(pt_row, p, page_size) : -1;
+    int p[kSlotsPer];
+#pragma unroll
+    for (int u = 0; u < kSlotsPer; ++u) {
+      const int i = tid + u * kThreads;
+      p[u] = (i < span && start + i < sel_stride) ? lst[start + i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kSlotsPer; ++u) {
+      const int li = start + tid + u * kThreads;
+      if (tid + u * kThreads >= len) p[u] = -1;
+      else if (li >= cnt) p[u] = extra_pos[(size_t)t * n_extra + (li - cnt)];
+    }
+    int pg[kSlotsPer];
+#pragma unroll
+    for (int u = 0; u < kSlotsPer; ++u) pg[u] = p[u] >= 0 ? pt_row[p[u] / page_size] : 0;
+#pragma unroll
+    for (int u = 0; u < kSlotsPer; ++u) {
+      const int i = tid + u * kThreads;
+      if (i < span) s_slot[i] = p[u] >= 0 ? pg[u] * page_size + p[u] % page_size : -1;
     }
   }
   __syncthreads();
@@ -339,15 +362,12 @@ combine_kernel(const float* __restrict__ part, int splits, uint16_t* __restrict_
 }  // namespace
 
 void attn_plan(int total_q, int n_extra, int* splits, int* split_len) {
-  const int bound = kMaxSel + n_extra;
-  const int step = kWaves * kChunk;                    // 128 positions
+  const int nchunk = (kMaxSel + n_extra + kChunk - 1) / kChunk;   // 32-position chunks
   const int pairs = total_q * kKVHeads;
   int s = (256 + pairs - 1) / pairs;     // about one 4-wave work group per CU
-  s = std::max(1, std::min(s, (bound + step - 1) / step));
-  int len = (bound + s - 1) / s;
-  len = ((len + step - 1) / step) * step;
-  *split_len = len;
-  *splits = (bound + len - 1) / len;
+  s = std::max(1, std::min(s, nchunk / kWaves));   // at least a chunk per wave
+  *splits = s;
+  *split_len = ((nchunk + s - 1) / s) * kChunk;   // the longest split
 }
 
 size_t attn_workspace_bytes(int total_q, int n_extra) {
@@ -362,8 +382,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   const int nblk = a.total_q * kKVHeads * a.splits;
   hipLaunchKernelGGL(attn_kernel, dim3(nblk), dim3(kThreads), 0, stream, a.q, a.q_req, a.k_pool,
                      a.v_pool, a.page_table, a.pt_stride, a.page_size, a.sel_pos, a.sel_count,
-                     a.sel_stride, a.extra_pos, a.n_extra, scale_log2, a.splits, a.split_len,
-                     a.part, a.out, a.lse);
+                     a.sel_stride, a.extra_pos, a.n_extra, scale_log2, a.splits, a.part, a.out, a.lse);
   if (a.splits > 1) {
     hipLaunchKernelGGL(combine_kernel, dim3(a.total_q * kKVHeads), dim3(256), 0, stream, a.part,
                        a.splits, a.out, a.lse);

@@ -65,7 +65,7 @@ struct AttnArgs {
   // workspace (split partials)
   float* part;               // [total_q, kv, splits, 8 + 8 + 8*256]
   int splits;
-  int split_len;             // positions per split (multiple of 128)
+  int split_len;             // positions of the longest split (multiple of 32)
 };
 void attn_plan(int total_q, int n_extra, int* splits, int* split_len);
 size_t attn_workspace_bytes(int total_q, int n_extra);
