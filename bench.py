@@ -10,6 +10,8 @@ pages.  --workload picks one of the other seeded workloads instead:
   prefill_chunk4096_prefix126976       4096 new tokens on a 126976-token prefix
   indexshare_b4_l262140                batch 4 at L = 262140: IndexShare reuse steps,
                                        with full decode steps timed beside them
+  verify_b32x4_loguniform_4k_128k      target verification: 4 query tokens per request
+                                       (capture token + 3 drafts), batch 32, seed 1006
 
 A step is one pass of the whole hot path for the batch: ingest the step's indexer
 keys (builder), score + top-512 + expansion (indexer), sparse GQA.  A reuse step
@@ -56,6 +58,11 @@ WORKLOADS = {
         kind="indexshare", steps=1000, warmup=20, sets=4,
         metric="QSA IndexShare reuse-step tokens/s, batch 4 at 262140 ctx (full decode step beside it)",
         context="262140"),
+    "verify_b32x4_loguniform_4k_128k": dict(
+        kind="verify", steps=1000, warmup=20, sets=4,
+        metric="QSA target-verify tokens/s, batch 32 x 4 query tokens, log-uniform 4K-128K ctx; "
+               "HBM GB/s vs peak",
+        context="log-uniform 4096..131072, 4 query tokens per request"),
 }
 
 _CSRC = "block_sparse_attention_c4_amd/csrc/"
@@ -69,6 +76,9 @@ ENTRY = {"build": "qsa_build_index_keys", "index": "qsa_index_topk", "attend": "
 
 
 def stage_kernels(kind: str) -> dict:
+    if kind == "verify":
+        return {"build": "build_kernel", "index": "score_multi_kernel + topk_kernel",
+                "attend": "attn_kernel + combine_kernel"}
     if kind == "prefill":
         return {"build": "build_kernel",
                 "index": "score_mfma_kernel + topk_codes_kernel (+ rescore_kernel, topk_queued_kernel)",
@@ -98,6 +108,28 @@ def decode_bytes(wl, counts: np.ndarray, n_extra: int = 0) -> dict:
     att = counts + n_extra
     attend = int(np.sum(2 * 2 * 256 * 2 * att + 4 * att + 4 + 16 * 256 * 2 * 2 + 16 * 4))
     return {"build": build, "index": index, "attend": attend, "step": build + index + attend}
+
+
+def verify_bytes(wl, sel_pos: np.ndarray, counts: np.ndarray) -> dict:
+    """Bytes each stage must move (read + write) for a batch with a few query tokens
+    per request.  Counted: the new raw keys and the compressed keys of blocks they
+    complete; each request's visible compressed keys once (its queries share them),
+    each query's indexer query, weights and written selection; K and V of the union
+    of the positions a request's queries attend (both KV heads), each query's
+    position list, query and output.  Not counted: scratch scores, split partials
+    and re-reads."""
+    p = wl.q_pos.astype(np.int64)
+    n_new = int(np.sum(wl.lengths - wl.prefix_len))
+    completed = int(np.sum(wl.lengths // 4 - wl.prefix_len // 4))
+    build = n_new * 256 + completed * (256 + 3 * 256)
+    index = int(256 * np.sum(wl.lengths // 4)) + int(np.sum(4 * 128 * 2 + 16 + 512 * 4 + 4 * counts + 4))
+    unique = 0
+    for b in range(wl.batch):
+        rows = np.nonzero(wl.q_req == b)[0]
+        unique += len(np.unique(np.concatenate([sel_pos[t, :counts[t]] for t in rows])))
+    attend = 2 * 2 * 256 * 2 * unique + int(np.sum(4 * counts + 4 + 16 * 256 * 2 * 2 + 16 * 4))
+    return {"build": build, "index": index, "attend": attend, "step": build + index + attend,
+            "unique_positions": unique, "positions": int(np.sum(counts))}
 
 
 def prefill_work(wl, counts: np.ndarray) -> dict:
@@ -338,7 +370,31 @@ def main() -> int:
     sets = [base] + [base.replicate() for _ in range(nsets - 1)]
     for d in sets:
         d.ws_attn.zero_()
-    base.step()
+    # A chunk that starts inside a block reads that block's older tokens from the
+    # 4-slot ring and leaves the tokens of its own last, unfinished block in the same
+    # slots, so a repeated step would read the newer tokens.  Where that happens
+    # (target verification at arbitrary lengths) every step first restores the
+    # ring: a device copy of 1 KB per request, counted in the step.
+    restore = kind == "verify"
+    if restore:
+        for d in sets:
+            d.ring_saved = d.ring.clone()
+
+    def step_fn(d):
+        if not restore:
+            return d.step
+
+        def run():
+            d.ring.copy_(d.ring_saved)
+            d.step()
+        return run
+
+    def build_fn(d):
+        if restore:
+            d.ring.copy_(d.ring_saved)
+        d.build_step()
+
+    step_fn(base)()
     torch.cuda.synchronize()
     counts = base.sel_count.cpu().numpy().astype(np.int64)
     ref_out = base.out.clone()
@@ -358,10 +414,9 @@ def main() -> int:
         return time_loop(torch, fns, graph, steps, warmup), launch
 
     # ---------------- whole steps
-    ms_step, launch = timed([d.step for d in sets], [d.out for d in sets], [ref_out] * len(sets))
+    ms_step, launch = timed([step_fn(d) for d in sets], [d.out for d in sets], [ref_out] * len(sets))
     assert torch.equal(sets[(steps - 1) % len(sets)].out, ref_out)
-    stages = [("build", lambda d: d.build_step()), ("index", lambda d: d.index()),
-              ("attend", lambda d: d.attend())]
+    stages = [("build", build_fn), ("index", lambda d: d.index()), ("attend", lambda d: d.attend())]
     stage_us = time_stages(torch, sets, stages, K)
 
     # ---------------- IndexShare: reuse steps j = 1..3 cycled over the input copies
@@ -445,6 +500,22 @@ def main() -> int:
                               "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                               "frac": round(achieved / HBM_PEAK_GBPS, 4),
                               "traffic": load_traffic(args.workload, "attend")}
+    elif kind == "verify":
+        nbytes = verify_bytes(wl, base.sel_pos.cpu().numpy(), counts)
+        config["query_tokens_per_request"] = int(wl.total_q // wl.batch)
+        config["step_includes"] = "a device copy restoring the pending-token ring (1 KB per request)"
+        result["value"] = round(wl.total_q / (ms_step * 1e-3), 1)
+        result["ms_per_step"] = round(ms_step, 5)
+        result["step_hbm_gbps"] = round(nbytes["step"] / (ms_step * 1e-3) / 1e9, 1)
+        result["step_hbm_frac"] = round(nbytes["step"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+        result["algorithmic_bytes"] = nbytes
+        dom = max(("build", "index", "attend"), key=lambda k: stage_us[k])
+        achieved = nbytes[dom] / (stage_us[dom] * 1e-6) / 1e9
+        entry = "qsa_sparse_gqa_prefill" if dom == "attend" else ENTRY[dom]
+        result["roofline"] = {"bound": "hbm", "kernel": kernels[dom], "entry_point": entry,
+                              "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                              "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                              "traffic": load_traffic(args.workload, dom)}
     else:
         nbytes = decode_bytes(wl, counts)
         result["value"] = round(wl.batch / (ms_step * 1e-3), 1)

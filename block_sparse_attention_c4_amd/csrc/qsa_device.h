@@ -69,6 +69,15 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// Max over the 16 lanes of a row; every lane of the row receives it.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0xb1>(v));
+  v = fmaxf(v, dpp_f<0x4e>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return v;
+}
+
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
 // Value of lane ^ 16 / lane ^ 32, on the VALU (gfx950 v_permlane16/32_swap): swapping
@@ -118,6 +127,23 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   v = min(v, (uint32_t)dpp_i<0x140, 0xf>((int)v));
   v = min(v, lane_xor16_u32(v));
   return min(v, lane_xor32_u32(v));
+}
+
+// max(0, x) as an integer max on the bits: negative values and -0 become +0.
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// Block score from the 4 head dots: sum_h w_h * max(0, d_h), in a fixed order.  The
+// sum starts from +0 and every term adds a product onto it, so a zero score is +0
+// and equal scores have equal keys.  Every MFMA scorer uses this function, so equal
+// operands give bit-identical scores.
+__device__ __forceinline__ float head_mix(f32x4_t d, const float (&w)[kIdxHeads]) {
+  float s = fmaf(w[0], relu_bits(d[0]), 0.f);   // +0 addend: a zero product gives +0
+  s = fmaf(w[1], relu_bits(d[1]), s);
+  s = fmaf(w[2], relu_bits(d[2]), s);
+  s = fmaf(w[3], relu_bits(d[3]), s);
+  return s;
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }

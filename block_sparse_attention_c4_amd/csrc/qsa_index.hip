@@ -1,4 +1,5 @@
-// Stage 2a: indexer block scores (decode).
+// Stage 2a: indexer block scores for decode-like batches (paged GEMV) and for a
+// few queries per request (multi-query MFMA scorer).
 //
 // [SGLang day-0 post on Qwen3.8-Flash-Next, section "Qwen Sparse Attention:
 // Retrieve Coarsely, Attend Precisely"]: a query scores every visible compressed
@@ -9,7 +10,12 @@
 // (one 4 KB compressed page when page_size = 64): 4 loads of 16 B per lane, each
 // load covering 4 blocks x 256 B contiguous.  Lane l owns dims (l%16)*8 .. +8 of
 // block (l/16); the dot products use v_dot2_f32_bf16 (bf16 pairs, FP32
-// accumulation) and are summed over the 16 lanes of a row with DPP.  Top-512
+// accumulation) and are summed over the 16 lanes of a row with DPP.
+//
+// score_multi_kernel serves batches with a few queries per request, such as the
+// verification pass over drafted tokens [same post, section "IndexShare MTP:
+// Reusing the QSA Selection Across Draft Steps": the target model checks N+1
+// tokens per request]: the queries of a request share each key load.  Top-512
 // selection and expansion live in qsa_topk.hip.
 #include "qsa_device.h"
 #include "qsa_launch.h"
@@ -195,6 +201,194 @@ score_kernel(int nq, const uint16_t* __restrict__ idx_q, const float* __restrict
   }
 }
 
+// ------------------------------------------------------------------ multi-query scorer
+
+// A few queries per request: target verification of drafted tokens, small chunks.
+// Queries are taken in windows of 4 consecutive ones.  The queries of a window that
+// share a request form a pass, and a pass scores each 16-block group of its request
+// once for all its queries, on MFMA: A = 4 queries x 4 heads (16 rows; rows of
+// queries outside the pass are zero), B = the group's 16 keys (k = dims).  Lane l
+// of the result holds the 4 head dots of query l/16 and block l%16.
+//
+// One wave per work group; a launch covers up to 64 windows, one per lane.  Units
+// (window, pass, group) are flattened and each wave takes a contiguous range.  The
+// loop requests page-table entries two units ahead and keys (plus the pass's query
+// rows when the pass changes) one unit ahead.  A unit's scores are stored after the
+// next unit's loads have been issued, so a wait never covers a store issued less
+// than a unit earlier.
+constexpr int kWin = 4;
+constexpr int kMultiWindows = 64;
+
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+struct Unit {
+  int win, j, g;        // window (lane), leader query of the pass, group
+  int mask;             // the pass's queries in the window (4 bits)
+  int nc_max;           // visible blocks of the pass's longest query
+  const int32_t* pt_row;
+};
+
+struct PassRows {
+  u32x4_t af[4];        // A operand: query (l%16)/4, head l%4, dims 8(l/16) + 32kc
+  float w[kIdxHeads];   // weights of this lane's result query l/16
+  int nc;               // its visible blocks (0 when it is not in the pass)
+  int t;                // its query index in the launch
+};
+
+__global__ void __launch_bounds__(64, 4)   // 4 waves per SIMD
+score_multi_kernel(int nq, const uint16_t* __restrict__ idx_q, const float* __restrict__ idx_w,
+                   const int32_t* __restrict__ q_req, const int32_t* __restrict__ q_pos,
+                   const int32_t* __restrict__ page_table, int pt_stride, int page_size,
+                   const uint16_t* __restrict__ comp, float* __restrict__ scores, int score_stride,
+                   float* __restrict__ gmax) {
+  // per window: requests, visible blocks, and per pass leader j its queries (4 bits)
+  // and visible blocks of its longest query (0: j leads no pass)
+  __shared__ int s_req[kMultiWindows][kWin], s_nc[kMultiWindows][kWin];
+  __shared__ int s_pnc[kMultiWindows][kWin], s_pmask[kMultiWindows];
+  const int lane = threadIdx.x;
+  int mine = 0;
+  {
+    int wreq[kWin], wnc[kWin];
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) {
+      const int t = kWin * lane + j;
+      wreq[j] = t < nq ? q_req[t] : -1;
+      wnc[j] = t < nq ? (q_pos[t] + 1) / kBlock : 0;
+      s_req[lane][j] = wreq[j];
+      s_nc[lane][j] = wnc[j];
+    }
+    int pmask = 0;
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) {
+      bool leader = wreq[j] >= 0;
+#pragma unroll
+      for (int i = 0; i < j; ++i) leader = leader && wreq[i] != wreq[j];
+      int m = 0, ncm = 0;
+#pragma unroll
+      for (int i = j; i < kWin; ++i)
+        if (wreq[i] == wreq[j]) {
+          m |= 1 << i;
+          ncm = max(ncm, wnc[i]);
+        }
+      pmask |= (leader ? m : 0) << (4 * j);
+      s_pnc[lane][j] = leader ? ncm : 0;
+      mine += leader ? (ncm + kScoreGroup - 1) / kScoreGroup : 0;
+    }
+    s_pmask[lane] = pmask;
+  }
+  __syncthreads();
+  const int incl = wave_inclusive_sum(mine);
+  const int excl = incl - mine;
+  const int total = __shfl(incl, 63, 64);
+  const int wave = blockIdx.x, nwaves = gridDim.x;
+  const int g_begin = (int)(((int64_t)total * wave) / nwaves);
+  const int ng = (int)(((int64_t)total * (wave + 1)) / nwaves) - g_begin;
+  if (ng <= 0) return;
+  const int bpp = page_size / kBlock;
+  const int gstride = score_stride / kScoreGroup;
+
+  auto groups = [](int nc) { return (nc + kScoreGroup - 1) / kScoreGroup; };
+  auto unit = [&](int i) {             // unit g_begin + i: i wave-uniform, every lane active;
+    Unit u;                            // every field is wave-uniform (scalar registers)
+    const int gi = g_begin + i;
+    u.win = __builtin_amdgcn_readfirstlane(__popcll(__ballot(incl <= gi)));
+    int local = __builtin_amdgcn_readfirstlane(gi - __shfl(excl, u.win, 64));
+    const int G0 = groups(s_pnc[u.win][0]), G1 = groups(s_pnc[u.win][1]), G2 = groups(s_pnc[u.win][2]);
+    int j = 0;
+    if (local >= G0) {
+      local -= G0;
+      j = 1;
+      if (local >= G1) {
+        local -= G1;
+        j = 2;
+        if (local >= G2) {
+          local -= G2;
+          j = 3;
+        }
+      }
+    }
+    u.j = __builtin_amdgcn_readfirstlane(j);
+    u.g = __builtin_amdgcn_readfirstlane(local);
+    u.mask = __builtin_amdgcn_readfirstlane((s_pmask[u.win] >> (4 * u.j)) & 15);
+    u.nc_max = __builtin_amdgcn_readfirstlane(s_pnc[u.win][u.j]);
+    u.pt_row = page_table + (size_t)__builtin_amdgcn_readfirstlane(s_req[u.win][u.j]) * pt_stride;
+    return u;
+  };
+  auto block_of = [&](const Unit& u) { return min(u.g * kScoreGroup + (lane & 15), u.nc_max - 1); };
+  auto pt_load = [&](const Unit& u) { return u.pt_row[block_of(u) / bpp]; };
+  auto key_load = [&](const Unit& u, int pg, u32x4_t (&kf)[4]) {
+    const int c = block_of(u);
+    const uint16_t* krow = comp + ((int64_t)pg * bpp + (c % bpp)) * kIdxDim + 8 * (lane >> 4);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) kf[kc] = ld16(krow + 32 * kc);
+  };
+  auto pass_load = [&](const Unit& u, PassRows& r) {
+    const int qa = (lane & 15) >> 2;   // A row query
+    const int ta = kWin * u.win + qa;
+    const bool ina = (u.mask >> qa) & 1;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+      r.af[kc] = ina ? ld16(idx_q + ((size_t)ta * kIdxHeads + (lane & 3)) * kIdxDim + 32 * kc +
+                            8 * (lane >> 4))
+                     : u32x4_t{0u, 0u, 0u, 0u};
+    const int qd = lane >> 4;          // result query
+    r.t = kWin * u.win + qd;
+    const bool ind = (u.mask >> qd) & 1;
+    r.nc = ind ? s_nc[u.win][qd] : 0;
+#pragma unroll
+    for (int h = 0; h < kIdxHeads; ++h) r.w[h] = ind ? idx_w[(size_t)r.t * kIdxHeads + h] : 0.f;
+  };
+  auto same_pass = [](const Unit& a, const Unit& b) { return a.win == b.win && a.j == b.j; };
+  auto compute_store = [&](const Unit& u, const u32x4_t (&kf)[4], const PassRows& r) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) acc = mfma16(r.af[kc], kf[kc], acc);
+    const float s = head_mix(acc, r.w);
+    const int c = u.g * kScoreGroup + (lane & 15);
+    const bool ok = c < r.nc;
+    const float m = row16_max(ok ? s : -INFINITY);
+    if (ok) scores[(size_t)r.t * score_stride + c] = s;
+    if ((lane & 15) == 0 && u.g * kScoreGroup < r.nc) gmax[(size_t)r.t * gstride + u.g] = m;
+  };
+
+  // units i (even) and i+1 (odd) alternate between two register sets
+  Unit ua = unit(0), ub = ua, uc = ua, ud = ua;
+  PassRows r0, r1;
+  u32x4_t k0[4], k1[4];
+  int pg0 = pt_load(ua), pg1 = 0;
+  pass_load(ua, r0);
+  if (ng > 1) {
+    ub = unit(1);
+    pg1 = pt_load(ub);
+  }
+  key_load(ua, pg0, k0);
+  for (int i = 0; i < ng; i += 2) {
+    if (i + 2 < ng) {
+      uc = unit(i + 2);
+      pg0 = pt_load(uc);
+    }
+    if (i + 1 < ng) {
+      if (same_pass(ub, ua)) r1 = r0; else pass_load(ub, r1);
+      key_load(ub, pg1, k1);
+    }
+    compute_store(ua, k0, r0);
+    if (i + 1 >= ng) break;
+    if (i + 3 < ng) {
+      ud = unit(i + 3);
+      pg1 = pt_load(ud);
+    }
+    if (i + 2 < ng) {
+      if (same_pass(uc, ub)) r0 = r1; else pass_load(uc, r0);
+      key_load(uc, pg0, k0);
+    }
+    compute_store(ub, k1, r1);
+    ua = uc;
+    ub = ud;
+  }
+}
+
 }  // namespace
 
 // Workspace: FP32 score rows [total_q, stride], then FP32 group maxima
@@ -224,22 +418,41 @@ void index_workspace_carve(IndexArgs& a, void* ws) {
   a.queue = reinterpret_cast<int*>(base + rows);
 }
 
-// Decode-like batches (about one query per request) take the paged GEMV scorer and
-// the latency-oriented select; chunks of many queries per request share their keys
-// and take the MFMA scorer.
+// Decode-like batches (about one query per request) take the paged GEMV scorer;
+// a few queries per request (2 to 15 on average) take the multi-query MFMA scorer;
+// both feed the FP32 select.  Chunks of many queries per request share their keys
+// over 64-query tiles and take the MFMA scorer with the code-based select.
 static bool use_mfma(const IndexArgs& a) {
-  return a.total_q >= 64 && a.total_q >= 4 * a.batch;
+  return a.total_q >= 64 && a.total_q >= 16 * a.batch;
 }
+static bool use_multi(const IndexArgs& a) { return a.total_q >= 2 * a.batch; }
 
 hipError_t launch_index(const IndexArgs& a, hipStream_t stream) {
   if (use_mfma(a)) return launch_index_mfma(a, stream);
+  const int64_t gpq = (a.max_pos / kBlock + kScoreGroup - 1) / kScoreGroup;   // groups per query, bound
+  if (use_multi(a)) {
+    constexpr int kQPerLaunch = kWin * kMultiWindows;
+    for (int q0 = 0; q0 < a.total_q; q0 += kQPerLaunch) {
+      const int nq = std::min(kQPerLaunch, a.total_q - q0);
+      // passes: one per window, plus one per request boundary inside a window
+      const int64_t passes = std::min<int64_t>(nq, (nq + kWin - 1) / kWin + a.batch - 1);
+      const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(passes * gpq / 2, 4096));
+      hipLaunchKernelGGL(score_multi_kernel, dim3(grid), dim3(64), 0, stream, nq,
+                         a.idx_q + (size_t)q0 * kIdxHeads * kIdxDim,
+                         a.idx_w + (size_t)q0 * kIdxHeads, a.q_req + q0, a.q_pos + q0,
+                         a.page_table, a.pt_stride, a.page_size, a.comp,
+                         a.scores + (size_t)q0 * a.score_stride, a.score_stride,
+                         a.gmax_f + (size_t)q0 * (a.score_stride / kScoreGroup));
+    }
+    launch_topk(a, stream);
+    return hipGetLastError();
+  }
   constexpr int kQPerLaunch = 64;
   for (int q0 = 0; q0 < a.total_q; q0 += kQPerLaunch) {
     const int nq = std::min(kQPerLaunch, a.total_q - q0);
     // the block counts are only known on the device: size the grid by the bound,
     // at most 16 waves per CU
-    const int64_t groups_bound =
-        (int64_t)nq * ((a.max_pos / kBlock + kScoreGroup - 1) / kScoreGroup);
+    const int64_t groups_bound = (int64_t)nq * gpq;
     // at most kWaveGroups groups per wave; at most 16 waves per CU otherwise
     const int64_t want = std::min<int64_t>(groups_bound / 2, 4096);
     const int grid = (int)std::max<int64_t>(

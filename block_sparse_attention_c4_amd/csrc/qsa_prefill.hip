@@ -39,22 +39,6 @@ __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
-// max(0, x) as an integer max on the bits: negative values and -0 become +0.
-__device__ __forceinline__ float relu_bits(float x) {
-  return __int_as_float(max(__float_as_int(x), 0));
-}
-
-// sum_h w_h * max(0, d_h) in a fixed order.  The sum starts from +0 and every term
-// adds a product onto it, so a zero score is +0 and equal scores have equal keys.  Every kernel that scores uses this function, so
-// equal operands give bit-identical scores.
-__device__ __forceinline__ float head_mix(f32x4_t d, const float (&w)[kIdxHeads]) {
-  float s = fmaf(w[0], relu_bits(d[0]), 0.f);   // +0 addend: a zero product gives +0
-  s = fmaf(w[1], relu_bits(d[1]), s);
-  s = fmaf(w[2], relu_bits(d[2]), s);
-  s = fmaf(w[3], relu_bits(d[3]), s);
-  return s;
-}
-
 // Top 16 bits of the order-preserving key of a score.
 __device__ __forceinline__ uint32_t score_code(float s) {
   const uint32_t u = __float_as_uint(s);

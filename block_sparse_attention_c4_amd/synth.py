@@ -272,10 +272,19 @@ def indexshare_b4_l262140(seed: int = 1005) -> Workload:
                          page_order="shuffled", reuse_steps=3)
 
 
+def verify_b32_loguniform(seed: int = 1006) -> Workload:
+    """Target verification of drafted tokens: batch 32, 4 query tokens per request (the
+    capture token plus 3 drafts) at the end of a cache of log-uniform length in
+    [4096, 131072]; every query has its own selection."""
+    return make_workload("verify_b32x4_loguniform_4k_128k", "prefill", seed, None, chunk=4,
+                         page_order="shuffled", draw_lengths=_loguniform_lengths(32, 4096, 131072))
+
+
 FULL_SIZE = {
     "decode_b1_l4099": decode_b1_l4099,
     "decode_b8_l32k": decode_b8_l32k,
     "decode_b32_loguniform_4k_128k": decode_b32_mixed,
     "prefill_chunk4096_prefix126976": prefill_4096_on_126976,
     "indexshare_b4_l262140": indexshare_b4_l262140,
+    "verify_b32x4_loguniform_4k_128k": verify_b32_loguniform,
 }

@@ -57,10 +57,25 @@ SMALL = {
     "decode_batch70": lambda: synth.make_workload(
         "decode_batch70", "decode", 305,
         [3, 700, 2051, 40000] + [1 + (i * 7919) % 20000 for i in range(66)], hot_per_req=2),
-    # a prefill chunk of fewer than 64 queries: the paged-GEMV scorer and the FP32
-    # select, with 20 queries per request
+    # a prefill chunk of fewer than 64 queries: the multi-query scorer (5 windows of
+    # 4 queries per request) and the FP32 select
     "prefill_small_chunk": lambda: synth.make_workload(
         "prefill_small_chunk", "prefill", 306, [5000, 40000], chunk=20),
+    # target verification, 4 query tokens per request: the multi-query scorer with one
+    # pass per window.  Lengths cover queries with no visible block, n_c around 512,
+    # the direct and the group-maximum select, page 16
+    "verify_ragged": lambda: synth.make_workload(
+        "verify_ragged", "prefill", 312,
+        [4, 7, 2052, 2055, 4100, 9003, 33001, 40000, 701, 2100, 16, 70001], chunk=4,
+        hot_per_req=2),
+    "verify_page16": lambda: synth.make_workload(
+        "verify_page16", "prefill", 313, [2050, 9000, 35003, 64], chunk=4, page_size=16),
+    # 3 queries per request: windows of 4 straddle requests (two passes per window)
+    "verify_chunk3": lambda: synth.make_workload(
+        "verify_chunk3", "prefill", 314, [3 + (i * 2741) % 12000 for i in range(21)], chunk=3),
+    # 70 requests x 4 queries: more than the 256 queries of one multi-query launch
+    "verify_batch70": lambda: synth.make_workload(
+        "verify_batch70", "prefill", 315, [4 + (i * 7919) % 6000 for i in range(70)], chunk=4),
 }
 
 
@@ -191,6 +206,14 @@ def test_index_prefill_all_ties():
     # many queries, every score 0: each row is handed from the code-based select to
     # the FP32 select, which keeps the 512 lowest blocks
     wl = synth.make_workload("ties_prefill", "prefill", 310, [9000, 40000], chunk=48)
+    wl.idx_q[:] = 0
+    _check_index_stage(wl)
+
+
+def test_index_verify_all_ties():
+    # 4 queries per request with zero indexer queries: the multi-query scorer writes
+    # +0 for every block, and the FP32 select keeps the 512 lowest blocks
+    wl = synth.make_workload("ties_verify", "prefill", 316, [9000, 40000, 2100, 7], chunk=4)
     wl.idx_q[:] = 0
     _check_index_stage(wl)
 
