@@ -114,6 +114,10 @@ class Workload:
     reuse_q: np.ndarray | None = None                # [steps, B, 16, 256] uint16 (indexshare)
     reuse_steps: int = 0
     rope_theta: float = ROPE_THETA
+    k_pool_fp8: np.ndarray | None = None             # FP8 E4M3 codes of the pools (uint8), and
+    v_pool_fp8: np.ndarray | None = None             # their per-pool scales
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def batch(self) -> int:
@@ -226,6 +230,25 @@ def make_workload(name: str, kind: str, seed: int, lengths, *, hot_per_req: int 
                     prefix_len=prefix.astype(np.int64), hot_blocks=hot_blocks,
                     reuse_q=reuse_q, reuse_steps=reuse_steps if kind == "indexshare" else 0,
                     rope_theta=rope_theta)
+
+
+def with_fp8_kv(wl: Workload) -> Workload:
+    """Add FP8 E4M3 copies of the K/V pools: each pool's bf16 values divided by one
+    scale (its largest magnitude / 448) and rounded to nearest even by torch's
+    float8_e4m3fn conversion."""
+    import torch
+
+    def quantize(pool_bits):
+        x = torch.from_numpy(bf16_bits_to_f32(pool_bits))
+        scale = float(x.abs().max()) / 448.0
+        if scale == 0.0:
+            scale = 1.0
+        codes = (x / scale).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        return codes, scale
+
+    wl.k_pool_fp8, wl.k_scale = quantize(wl.k_pool)
+    wl.v_pool_fp8, wl.v_scale = quantize(wl.v_pool)
+    return wl
 
 
 # --- the five workloads at full size ------------------------------------------------

@@ -4,14 +4,17 @@ Only the tests, the smoke check and the CPU-baseline leg of the benchmark may
 import this module. The library path never does: it shares no code, constants,
 tables or helpers with the HIP kernels, and it reads no value they produce.
 
-Everything is computed from the bf16 input bits in float64, except the one step
-whose precision the pages fix (the block mean is taken in FP32).
+Everything is computed from the bf16 input bits (or FP8 K/V codes) in float64,
+except the one step whose precision the pages fix (the block mean is taken in
+FP32).
 
 Sources, cited by title and section:
   [QSA]  SGLang day-0 post on Qwen3.8-Flash-Next, section "Qwen Sparse Attention:
          Retrieve Coarsely, Attend Precisely".
   [IS]   same post, section "IndexShare MTP: Reusing the QSA Selection Across
          Draft Steps"; and its "Model Architecture" list, IndexShare MTP item.
+  [AIL]  ailone.io model page on Qwen3.8-Flash-Next, its comparison of vLLM builds:
+         a K/V cache in FP8 at the speed of BF16 with a larger token pool.
 
 Readings where the pages are silent or garbled (each is listed in the design doc):
   R1  The scoring formula is cut off in [QSA]; the score of block c for a query is
@@ -30,6 +33,10 @@ Readings where the pages are silent or garbled (each is listed in the design doc):
       1/sqrt(256); no sink, soft-cap or output gate; lse is the natural log.
   R8  IndexShare: reuse step j attends to the captured positions plus p_cap+1 ..
       p_cap+j (the positions drafted since the capture).
+  R9  FP8 K/V [AIL] (format and scaling not stated): OCP FP8 E4M3 codes (bias 7, 3
+      mantissa bits, no infinities, S.1111.111 is NaN, largest finite 448) with one
+      scale per pool; a stored code c stands for e4m3(c) * k_scale (K) or
+      e4m3(c) * v_scale (V).  Attention is then as in R7 on those values.
   parity unpinned: fidelity to the real model's readings R1, R3 (pairing, rotary
   fraction, theta) and R2's epsilon cannot be checked against the pages.
 """
@@ -50,6 +57,21 @@ def bf16_to_f64(bits) -> np.ndarray:
     """bf16 bit patterns -> float64 (exact)."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
     return b.view(np.float32).astype(np.float64)
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """OCP FP8 E4M3 codes -> float64 (exact), reading R9.
+
+    A code is sign s, exponent e (4 bits, bias 7) and mantissa m (3 bits): e > 0
+    gives (-1)^s * (1 + m/8) * 2^(e-7); e = 0 gives (-1)^s * (m/8) * 2^-6; the
+    all-ones exponent and mantissa (0x7f, 0xff) are NaN.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e > 0, (1.0 + m / 8.0) * np.exp2(e - 7.0), (m / 8.0) * 2.0 ** -6)
+    return np.where((c & 0x7F) == 0x7F, np.nan, s * mag)
 
 
 def round_to_bf16(x) -> np.ndarray:
@@ -188,9 +210,20 @@ def sparse_gqa(q_bits, k_rows_bits, v_rows_bits, sm_scale: float):
 
     q_bits: [Hq, D]; k_rows_bits, v_rows_bits: [n, Hkv, D] -> (out [Hq, D], lse [Hq]).
     """
-    q = bf16_to_f64(q_bits)
-    k = bf16_to_f64(k_rows_bits)
-    v = bf16_to_f64(v_rows_bits)
+    return attention_f64(bf16_to_f64(q_bits), bf16_to_f64(k_rows_bits),
+                         bf16_to_f64(v_rows_bits), sm_scale)
+
+
+def sparse_gqa_fp8(q_bits, k_rows_codes, v_rows_codes, k_scale: float, v_scale: float,
+                   sm_scale: float):
+    """sparse_gqa over FP8 K/V rows (reading R9): the codes decoded and scaled by
+    their pool's scale, then the same attention."""
+    return attention_f64(bf16_to_f64(q_bits), e4m3_to_f64(k_rows_codes) * k_scale,
+                         e4m3_to_f64(v_rows_codes) * v_scale, sm_scale)
+
+
+def attention_f64(q, k, v, sm_scale: float):
+    """Per-head softmax attention in float64 (R7): q [Hq, D], k and v [n, Hkv, D]."""
     hq, hkv = q.shape[0], k.shape[1]
     group = hq // hkv
     out = np.zeros_like(q)
@@ -212,37 +245,49 @@ def gather_rows(pool, page_row, positions, page_size: int):
 
 
 def query(comp_bits, idx_q_bits, idx_w, q_bits, p: int, page_row, k_pool, v_pool,
-          page_size: int, sm_scale: float, topk: int = TOPK_BLOCKS):
+          page_size: int, sm_scale: float, topk: int = TOPK_BLOCKS, kv_scales=None):
     """One query at position p through indexer and sparse GQA.
 
     comp_bits: the request's compressed keys in logical block order (at least
-    visible_blocks(p) rows).  Returns a dict with scores, sel_blocks, positions,
-    out and lse.
+    visible_blocks(p) rows).  k_pool / v_pool hold bf16 bits, or FP8 E4M3 codes when
+    kv_scales = (k_scale, v_scale) is given.  Returns a dict with scores,
+    sel_blocks, positions, out and lse.
     """
     n_c = visible_blocks(p)
     scores = score_blocks(idx_q_bits, idx_w, comp_bits[:n_c])
     sel = select_blocks(scores, topk)
     pos = expand_positions(sel, p)
-    out, lse = sparse_gqa(q_bits, gather_rows(k_pool, page_row, pos, page_size),
-                          gather_rows(v_pool, page_row, pos, page_size), sm_scale)
+    out, lse = attend_positions(q_bits, pos, page_row, k_pool, v_pool, page_size, sm_scale,
+                                kv_scales)
     return {"scores": scores, "sel_blocks": sel, "positions": pos, "out": out, "lse": lse}
 
 
+def attend_positions(q_bits, pos, page_row, k_pool, v_pool, page_size: int, sm_scale: float,
+                     kv_scales=None):
+    """Sparse GQA of one query over logical positions `pos` of its request."""
+    k = gather_rows(k_pool, page_row, pos, page_size)
+    v = gather_rows(v_pool, page_row, pos, page_size)
+    if kv_scales is None:
+        return sparse_gqa(q_bits, k, v, sm_scale)
+    return sparse_gqa_fp8(q_bits, k, v, kv_scales[0], kv_scales[1], sm_scale)
+
+
 def indexshare_step(captured_positions, p_cap: int, j: int, q_bits, page_row, k_pool,
-                    v_pool, page_size: int, sm_scale: float):
+                    v_pool, page_size: int, sm_scale: float, kv_scales=None):
     """Reuse step j of the draft loop [IS] (reading R8): the captured selection
     plus the positions drafted since, without running the indexer."""
     pos = np.concatenate([np.asarray(captured_positions, dtype=np.int64),
                           np.arange(p_cap + 1, p_cap + j + 1, dtype=np.int64)])
-    out, lse = sparse_gqa(q_bits, gather_rows(k_pool, page_row, pos, page_size),
-                          gather_rows(v_pool, page_row, pos, page_size), sm_scale)
+    out, lse = attend_positions(q_bits, pos, page_row, k_pool, v_pool, page_size, sm_scale,
+                                kv_scales)
     return {"positions": pos, "out": out, "lse": lse}
 
 
 # ---------------------------------------------------------------- workload drivers
 # These take any object with the fields of a synthetic workload (lengths,
 # page_table, page_size, raw_idx_k, idx_q, idx_w, q, q_req, q_pos, k_pool, v_pool,
-# rope_theta, prefix_len, reuse_q, reuse_steps).
+# rope_theta, prefix_len, reuse_q, reuse_steps; for kv = "fp8" also k_pool_fp8,
+# v_pool_fp8, k_scale, v_scale).
 
 def index_state(wl, b: int, length: int):
     return build_index_state(wl.raw_idx_k[b], length, wl.rope_theta)
@@ -254,13 +299,22 @@ def comp_cache_entries(wl, b: int, comp_bits):
     return comp_slot(wl.page_table[b], c, wl.page_size), comp_bits
 
 
-def run_queries(wl, rows=None, sm_scale: float = 1.0 / 16.0, topk: int = TOPK_BLOCKS):
+def kv_pools(wl, kv: str):
+    """The workload's K/V pools and scales for kv = "bf16" or "fp8" (R9)."""
+    if kv == "fp8":
+        return wl.k_pool_fp8, wl.v_pool_fp8, (wl.k_scale, wl.v_scale)
+    return wl.k_pool, wl.v_pool, None
+
+
+def run_queries(wl, rows=None, sm_scale: float = 1.0 / 16.0, topk: int = TOPK_BLOCKS,
+                kv: str = "bf16"):
     """Every (or the listed) query row of a decode / prefill / capture workload.
 
     The compressed keys a query sees are those of the request's complete blocks
     up to and including its own position; a block's key depends only on its own
     four tokens, so one build over the request's tokens serves every row.
     """
+    k_pool, v_pool, scales = kv_pools(wl, kv)
     rows = range(wl.total_q) if rows is None else rows
     comp_of = {}
     res = {}
@@ -270,18 +324,19 @@ def run_queries(wl, rows=None, sm_scale: float = 1.0 / 16.0, topk: int = TOPK_BL
         if b not in comp_of:
             comp_of[b], _ = index_state(wl, b, int(wl.lengths[b]))
         res[t] = query(comp_of[b], wl.idx_q[t], wl.idx_w[t], wl.q[t], p, wl.page_table[b],
-                       wl.k_pool, wl.v_pool, wl.page_size, sm_scale, topk)
+                       k_pool, v_pool, wl.page_size, sm_scale, topk, scales)
     return res
 
 
-def run_indexshare(wl, captured, sm_scale: float = 1.0 / 16.0):
+def run_indexshare(wl, captured, sm_scale: float = 1.0 / 16.0, kv: str = "bf16"):
     """Reuse steps 1..reuse_steps for every request, from the capture results
     `captured` (as returned by run_queries)."""
+    k_pool, v_pool, scales = kv_pools(wl, kv)
     res = {}
     for b in range(wl.batch):
         p_cap = int(wl.q_pos[b])
         for j in range(1, wl.reuse_steps + 1):
             res[(j, b)] = indexshare_step(captured[b]["positions"], p_cap, j,
-                                          wl.reuse_q[j - 1, b], wl.page_table[b], wl.k_pool,
-                                          wl.v_pool, wl.page_size, sm_scale)
+                                          wl.reuse_q[j - 1, b], wl.page_table[b], k_pool,
+                                          v_pool, wl.page_size, sm_scale, scales)
     return res

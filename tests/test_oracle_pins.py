@@ -308,6 +308,63 @@ def test_gqa_matches_torch_sdpa():
     np.testing.assert_allclose(out, ref, atol=1e-12)
 
 
+# ------------------------------------------------------------------ FP8 K/V (reading R9)
+
+def test_e4m3_decode_hand_values():
+    # 1.0 = 0.0111.000, 1.5 = 0.0111.100, 448 = 0.1111.110 (largest finite),
+    # 2^-6 = 0.0001.000 (smallest normal), 2^-9 = 0.0000.001 (smallest subnormal),
+    # 7 * 2^-9 = 0.0000.111, -1.0 = 1.0111.000, -0 = 1.0000.000, 0.1111.111 is NaN
+    codes = [0x38, 0x3C, 0x7E, 0x08, 0x01, 0x07, 0xB8, 0x80, 0x00, 0x7F, 0xFF]
+    want = [1.0, 1.5, 448.0, 2.0 ** -6, 2.0 ** -9, 7 * 2.0 ** -9, -1.0, -0.0, 0.0,
+            float("nan"), float("nan")]
+    got = O.e4m3_to_f64(codes)
+    for c, g, w in zip(codes, got, want):
+        if math.isnan(w):
+            assert math.isnan(g), hex(c)
+        else:
+            assert g == w and math.copysign(1.0, g) == math.copysign(1.0, w), hex(c)
+
+
+def test_e4m3_decode_matches_torch_on_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3_to_f64(codes)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+def test_fp8_gqa_single_position_and_scales():
+    # one position: every head returns v_scale * V and lse = sm_scale * k_scale * q.K
+    rng = np.random.default_rng(15)
+    q = bits(rng.standard_normal((16, 256)))
+    k = rng.integers(0, 0x7E, size=(1, 2, 256), dtype=np.uint8)
+    v = rng.integers(0, 0x7E, size=(1, 2, 256), dtype=np.uint8)
+    k[..., ::2] |= 0x80                     # negative values too
+    out, lse = O.sparse_gqa_fp8(q, k, v, 0.25, 3.0, 1 / 16)
+    kv = torch.from_numpy(k).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    vv = torch.from_numpy(v).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    qf = O.bf16_to_f64(q)
+    for h in range(16):
+        np.testing.assert_array_equal(out[h], 3.0 * vv[0, h // 8])
+        assert lse[h] == pytest.approx(float(qf[h] @ kv[0, h // 8]) * 0.25 / 16, abs=1e-12)
+
+
+def test_fp8_gqa_matches_torch_sdpa_on_decoded_values():
+    rng = np.random.default_rng(16)
+    q = bits(rng.standard_normal((16, 256)))
+    k = rng.integers(0, 256, size=(200, 2, 256), dtype=np.uint8)
+    v = rng.integers(0, 256, size=(200, 2, 256), dtype=np.uint8)
+    k[(k & 0x7F) == 0x7F] = 0x3F           # no NaN codes in an input
+    v[(v & 0x7F) == 0x7F] = 0x3F
+    out, _ = O.sparse_gqa_fp8(q, k, v, 0.01, 0.5, 1 / 16)
+    kf = torch.from_numpy(k).view(torch.float8_e4m3fn).to(torch.float64).numpy() * 0.01
+    vf = torch.from_numpy(v).view(torch.float8_e4m3fn).to(torch.float64).numpy() * 0.5
+    ref = _torch_sdpa(O.bf16_to_f64(q), kf, vf, 1 / 16)
+    np.testing.assert_allclose(out, ref, atol=1e-12)
+
+
 # ------------------------------------------------------------------ whole query
 
 def test_pipeline_equals_dense_causal_attention_when_few_blocks():
