@@ -12,6 +12,7 @@ pages.  --workload picks one of the other seeded workloads instead:
                                        with full decode steps timed beside them
   verify_b32x4_loguniform_4k_128k      target verification: 4 query tokens per request
                                        (capture token + 3 drafts), batch 32, seed 1006
+  decode_b32_loguniform_4k_128k_fp8kv  the headline decode with FP8 E4M3 K/V pools
 
 A step is one pass of the whole hot path for the batch: ingest the step's indexer
 keys (builder), score + top-512 + expansion (indexer), sparse GQA.  A reuse step
@@ -58,6 +59,11 @@ WORKLOADS = {
         kind="indexshare", steps=1000, warmup=20, sets=4,
         metric="QSA IndexShare reuse-step tokens/s, batch 4 at 262140 ctx (full decode step beside it)",
         context="262140"),
+    "decode_b32_loguniform_4k_128k_fp8kv": dict(
+        kind="decode", kv="fp8", source="decode_b32_loguniform_4k_128k", steps=2000, warmup=50, sets=4,
+        metric="QSA decode tokens/s at 128K ctx with an FP8 E4M3 K/V cache (indexer+top-k+sparse GQA); "
+               "HBM GB/s vs peak",
+        context="log-uniform 4096..131072"),
     "verify_b32x4_loguniform_4k_128k": dict(
         kind="verify", steps=1000, warmup=20, sets=4,
         metric="QSA target-verify tokens/s, batch 32 x 4 query tokens, log-uniform 4K-128K ctx; "
@@ -75,7 +81,7 @@ KERNEL_SOURCES = {
 ENTRY = {"build": "qsa_build_index_keys", "index": "qsa_index_topk", "attend": "qsa_sparse_gqa_decode"}
 
 
-def stage_kernels(kind: str) -> dict:
+def stage_kernels(kind: str, kv: str = "bf16") -> dict:
     if kind == "verify":
         return {"build": "build_kernel", "index": "score_multi_kernel + topk_kernel",
                 "attend": "attn_kernel + combine_kernel"}
@@ -84,7 +90,7 @@ def stage_kernels(kind: str) -> dict:
                 "index": "score_mfma_kernel + topk_codes_kernel (+ rescore_kernel, topk_queued_kernel)",
                 "attend": "attn_kernel + combine_kernel"}
     return {"build": "build_kernel", "index": "score_kernel + topk_kernel",
-            "attend": "attn_kernel + combine_kernel"}
+            "attend": "attn_kernel<fp8> + combine_kernel" if kv == "fp8" else "attn_kernel + combine_kernel"}
 
 
 def traffic_file(workload: str) -> str:
@@ -93,20 +99,20 @@ def traffic_file(workload: str) -> str:
 
 # ------------------------------------------------------------------ algorithmic work
 
-def decode_bytes(wl, counts: np.ndarray, n_extra: int = 0) -> dict:
+def decode_bytes(wl, counts: np.ndarray, n_extra: int = 0, kv_bytes: int = 2) -> dict:
     """Bytes each decode stage must move (read + write), per step.  Counted: the new
     indexer key, ring and compressed key traffic of the builder; the compressed
     keys of every visible block, the indexer query and weights, and the written
-    selection of the indexer; K and V of every attended position (both KV heads),
-    the position list, the query and the output of sparse GQA.  Not counted:
-    scratch scores, split partials and re-reads."""
+    selection of the indexer; K and V of every attended position (both KV heads, at
+    kv_bytes per element), the position list, the query and the output of sparse
+    GQA.  Not counted: scratch scores, split partials and re-reads."""
     p = wl.q_pos.astype(np.int64)
     n_c = (p + 1) // 4
     completes = ((p + 1) % 4) == 0
     build = int(np.sum(256 + np.where(completes, 3 * 256 + 256, 256)))
     index = int(np.sum(256 * n_c + 4 * 128 * 2 + 4 * 4 + 512 * 4 + 4 * counts + 4))
     att = counts + n_extra
-    attend = int(np.sum(2 * 2 * 256 * 2 * att + 4 * att + 4 + 16 * 256 * 2 * 2 + 16 * 4))
+    attend = int(np.sum(2 * 2 * 256 * kv_bytes * att + 4 * att + 4 + 16 * 256 * 2 * 2 + 16 * 4))
     return {"build": build, "index": index, "attend": attend, "step": build + index + attend}
 
 
@@ -185,7 +191,7 @@ def _oracle_keys_at(O, wl, b: int, prefix_keys, p: int):
     return np.concatenate([prefix_keys, blk])
 
 
-def cpu_baseline(wl, seconds: float) -> dict:
+def cpu_baseline(wl, seconds: float, kv: str = "bf16") -> dict:
     """The oracle on the same workload, single-threaded, for about `seconds`: decode
     queries over the batch, prefill query rows of the chunk, or IndexShare reuse
     steps.  The prefix keys are built untimed; for prefill the chunk's own
@@ -239,12 +245,13 @@ def cpu_baseline(wl, seconds: float) -> dict:
             return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
                     "sample": f"{done} IndexShare reuse steps (request x step) of the same workload, "
                               f"float64 numpy oracle, {el:.1f} s"}
+        k_pool, v_pool, scales = O.kv_pools(wl, kv)
         t0 = time.perf_counter()
         while True:
             for b in range(wl.batch):
                 p = int(wl.q_pos[b])
                 O.query(_oracle_keys_at(O, wl, b, prefix[b], p), wl.idx_q[b], wl.idx_w[b], wl.q[b], p,
-                        wl.page_table[b], wl.k_pool, wl.v_pool, wl.page_size, scale)
+                        wl.page_table[b], k_pool, v_pool, wl.page_size, scale, kv_scales=scales)
                 done += 1
             el = time.perf_counter() - t0
             if el >= seconds:
@@ -363,8 +370,11 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     torch.cuda.set_device(0)
-    wl = synth.FULL_SIZE[args.workload]()
-    base = runner.DeviceWorkload(wl, "cuda:0")
+    kv = cfg.get("kv", "bf16")
+    wl = synth.FULL_SIZE[cfg.get("source", args.workload)]()
+    if kv == "fp8":
+        synth.with_fp8_kv(wl)
+    base = runner.DeviceWorkload(wl, "cuda:0", kv=kv)
     base.build_prefix()
     torch.cuda.synchronize()
     sets = [base] + [base.replicate() for _ in range(nsets - 1)]
@@ -458,7 +468,7 @@ def main() -> int:
         torch.mul(a, 1.0, out=b)
         torch.cuda.synchronize()
 
-    kernels = stage_kernels(kind)
+    kernels = stage_kernels(kind, kv)
     config = {"workload": args.workload, "batch": wl.batch, "seed": wl.seed, "context": cfg["context"],
               "q_heads": 16, "kv_heads": 2, "head_dim": 256, "indexer": "4x128", "topk_blocks": 512,
               "page_size": wl.page_size, "input_sets": len(sets), "launch": launch}
@@ -509,7 +519,7 @@ def main() -> int:
         result["step_hbm_gbps"] = round(nbytes["step"] / (ms_step * 1e-3) / 1e9, 1)
         result["step_hbm_frac"] = round(nbytes["step"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
         result["algorithmic_bytes"] = nbytes
-        dom = max(("build", "index", "attend"), key=lambda k: stage_us[k])
+        dom = "attend"   # it holds the step's longest kernel (attn_kernel) and most of its bytes
         achieved = nbytes[dom] / (stage_us[dom] * 1e-6) / 1e9
         entry = "qsa_sparse_gqa_prefill" if dom == "attend" else ENTRY[dom]
         result["roofline"] = {"bound": "hbm", "kernel": kernels[dom], "entry_point": entry,
@@ -517,21 +527,24 @@ def main() -> int:
                               "frac": round(achieved / HBM_PEAK_GBPS, 4),
                               "traffic": load_traffic(args.workload, dom)}
     else:
-        nbytes = decode_bytes(wl, counts)
+        nbytes = decode_bytes(wl, counts, kv_bytes=1 if kv == "fp8" else 2)
+        if kv == "fp8":
+            config["kv_cache"] = "fp8 e4m3, one scale per pool"
         result["value"] = round(wl.batch / (ms_step * 1e-3), 1)
         result["ms_per_step"] = round(ms_step, 5)
         result["step_hbm_gbps"] = round(nbytes["step"] / (ms_step * 1e-3) / 1e9, 1)
         result["step_hbm_frac"] = round(nbytes["step"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
         result["algorithmic_bytes"] = nbytes
-        dom = max(("build", "index", "attend"), key=lambda k: stage_us[k])
+        dom = "attend"   # it holds the step's longest kernel (attn_kernel) and most of its bytes
         achieved = nbytes[dom] / (stage_us[dom] * 1e-6) / 1e9
-        result["roofline"] = {"bound": "hbm", "kernel": kernels[dom], "entry_point": ENTRY[dom],
+        entry = "qsa_sparse_gqa_decode_fp8" if (dom == "attend" and kv == "fp8") else ENTRY[dom]
+        result["roofline"] = {"bound": "hbm", "kernel": kernels[dom], "entry_point": entry,
                               "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                               "frac": round(achieved / HBM_PEAK_GBPS, 4),
                               "traffic": load_traffic(args.workload, dom)}
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, kv)
     print(json.dumps(result), flush=True)
     return 0
 

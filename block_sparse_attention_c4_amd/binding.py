@@ -33,7 +33,8 @@ QSA_MAX_CONTEXT = 262144
 QSA_MAX_EXTRA = 8
 
 EXPORTED = ["qsa_status_string", "qsa_workspace_bytes", "qsa_build_index_keys", "qsa_index_topk",
-            "qsa_sparse_gqa_decode", "qsa_sparse_gqa_prefill"]
+            "qsa_sparse_gqa_decode", "qsa_sparse_gqa_prefill", "qsa_sparse_gqa_decode_fp8",
+            "qsa_sparse_gqa_prefill_fp8"]
 
 
 class QsaError(RuntimeError):
@@ -83,6 +84,13 @@ def lib() -> ctypes.CDLL:
         L.qsa_sparse_gqa_prefill.restype = ctypes.c_int
         L.qsa_sparse_gqa_prefill.argtypes = [ctypes.POINTER(QsaDims), _I, _P, _P, _P, _P, _P, _I, _P,
                                              _P, _I, _P, _P, _P, _SZ, _P]
+        _F = ctypes.c_float
+        L.qsa_sparse_gqa_decode_fp8.restype = ctypes.c_int
+        L.qsa_sparse_gqa_decode_fp8.argtypes = [ctypes.POINTER(QsaDims), _I, _P, _P, _P, _F, _F, _P,
+                                                _I, _P, _P, _I, _P, _I, _P, _P, _P, _SZ, _P]
+        L.qsa_sparse_gqa_prefill_fp8.restype = ctypes.c_int
+        L.qsa_sparse_gqa_prefill_fp8.argtypes = [ctypes.POINTER(QsaDims), _I, _P, _P, _P, _P, _F, _F,
+                                                 _P, _I, _P, _P, _I, _P, _P, _P, _SZ, _P]
         _lib = L
     return _lib
 
@@ -155,3 +163,25 @@ def qsa_sparse_gqa_prefill(dims, total_q, q, q_req, k_pool, v_pool, page_table, 
                                       _ptr(sel_count), sel_stride, _ptr(out), _ptr(lse),
                                       _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "qsa_sparse_gqa_prefill")
+
+
+def qsa_sparse_gqa_decode_fp8(dims, batch, q, k_pool, v_pool, k_scale, v_scale, page_table, pt_stride,
+                              sel_pos, sel_count, sel_stride, extra_pos, n_extra, out, lse, workspace,
+                              ws_bytes, stream=None) -> None:
+    st = lib().qsa_sparse_gqa_decode_fp8(ctypes.byref(dims), batch, _ptr(q), _ptr(k_pool),
+                                         _ptr(v_pool), float(k_scale), float(v_scale),
+                                         _ptr(page_table), pt_stride, _ptr(sel_pos), _ptr(sel_count),
+                                         sel_stride, _ptr(extra_pos), n_extra, _ptr(out), _ptr(lse),
+                                         _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "qsa_sparse_gqa_decode_fp8")
+
+
+def qsa_sparse_gqa_prefill_fp8(dims, total_q, q, q_req, k_pool, v_pool, k_scale, v_scale, page_table,
+                               pt_stride, sel_pos, sel_count, sel_stride, out, lse, workspace,
+                               ws_bytes, stream=None) -> None:
+    st = lib().qsa_sparse_gqa_prefill_fp8(ctypes.byref(dims), total_q, _ptr(q), _ptr(q_req),
+                                          _ptr(k_pool), _ptr(v_pool), float(k_scale), float(v_scale),
+                                          _ptr(page_table), pt_stride, _ptr(sel_pos),
+                                          _ptr(sel_count), sel_stride, _ptr(out), _ptr(lse),
+                                          _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "qsa_sparse_gqa_prefill_fp8")

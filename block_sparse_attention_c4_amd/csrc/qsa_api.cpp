@@ -1,5 +1,6 @@
 // C ABI of the QSA c4 hot path: argument checks, workspace carving, launches.
 // The operations themselves are specified in include/qsa.h.
+#include <cmath>
 #include "qsa.h"
 
 #include <hip/hip_runtime.h>
@@ -125,14 +126,17 @@ int qsa_index_topk(const qsa_dims* dims, int32_t batch, int32_t total_q, const u
   return hip_status(qsa::launch_index(a, static_cast<hipStream_t>(stream)));
 }
 
+// fp8: the pools hold E4M3 codes scaled by k_scale / v_scale (finite and > 0).
 static int gqa_common(const qsa_dims* dims, int32_t total_q, const uint16_t* q,
-                      const int32_t* q_req, const uint16_t* k_pool, const uint16_t* v_pool,
-                      const int32_t* page_table, int32_t pt_stride, const int32_t* sel_pos,
-                      const int32_t* sel_count, int32_t sel_stride, const int32_t* extra_pos,
-                      int32_t n_extra, uint16_t* out, float* lse, void* workspace,
-                      size_t ws_bytes, void* stream) {
+                      const int32_t* q_req, const void* k_pool, const void* v_pool, bool fp8,
+                      float k_scale, float v_scale, const int32_t* page_table, int32_t pt_stride,
+                      const int32_t* sel_pos, const int32_t* sel_count, int32_t sel_stride,
+                      const int32_t* extra_pos, int32_t n_extra, uint16_t* out, float* lse,
+                      void* workspace, size_t ws_bytes, void* stream) {
   int st = check_dims(dims);
   if (st != QSA_OK) return st;
+  if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return QSA_E_SHAPE;
   if (total_q < 0 || pt_stride < 1 || sel_stride < 1 || n_extra < 0 || n_extra > QSA_MAX_EXTRA ||
       total_q > (1 << 24))
     return QSA_E_SHAPE;
@@ -155,6 +159,9 @@ static int gqa_common(const qsa_dims* dims, int32_t total_q, const uint16_t* q,
   a.q_req = q_req;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
+  a.fp8 = fp8;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.page_table = page_table;
   a.sel_pos = sel_pos;
   a.sel_count = sel_count;
@@ -172,9 +179,20 @@ int qsa_sparse_gqa_decode(const qsa_dims* dims, int32_t batch, const uint16_t* q
                           const int32_t* sel_count, int32_t sel_stride, const int32_t* extra_pos,
                           int32_t n_extra, uint16_t* out, float* lse, void* workspace,
                           size_t ws_bytes, void* stream) {
-  return gqa_common(dims, batch, q, nullptr, k_pool, v_pool, page_table, pt_stride, sel_pos,
-                    sel_count, sel_stride, extra_pos, n_extra, out, lse, workspace, ws_bytes,
-                    stream);
+  return gqa_common(dims, batch, q, nullptr, k_pool, v_pool, false, 1.f, 1.f, page_table,
+                    pt_stride, sel_pos, sel_count, sel_stride, extra_pos, n_extra, out, lse,
+                    workspace, ws_bytes, stream);
+}
+
+int qsa_sparse_gqa_decode_fp8(const qsa_dims* dims, int32_t batch, const uint16_t* q,
+                              const uint8_t* k_pool, const uint8_t* v_pool, float k_scale,
+                              float v_scale, const int32_t* page_table, int32_t pt_stride,
+                              const int32_t* sel_pos, const int32_t* sel_count, int32_t sel_stride,
+                              const int32_t* extra_pos, int32_t n_extra, uint16_t* out, float* lse,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  return gqa_common(dims, batch, q, nullptr, k_pool, v_pool, true, k_scale, v_scale, page_table,
+                    pt_stride, sel_pos, sel_count, sel_stride, extra_pos, n_extra, out, lse,
+                    workspace, ws_bytes, stream);
 }
 
 int qsa_sparse_gqa_prefill(const qsa_dims* dims, int32_t total_q, const uint16_t* q,
@@ -183,8 +201,21 @@ int qsa_sparse_gqa_prefill(const qsa_dims* dims, int32_t total_q, const uint16_t
                            const int32_t* sel_count, int32_t sel_stride, uint16_t* out,
                            float* lse, void* workspace, size_t ws_bytes, void* stream) {
   if (total_q > 0 && !q_req) return QSA_E_NULL;
-  return gqa_common(dims, total_q, q, q_req, k_pool, v_pool, page_table, pt_stride, sel_pos,
-                    sel_count, sel_stride, nullptr, 0, out, lse, workspace, ws_bytes, stream);
+  return gqa_common(dims, total_q, q, q_req, k_pool, v_pool, false, 1.f, 1.f, page_table,
+                    pt_stride, sel_pos, sel_count, sel_stride, nullptr, 0, out, lse, workspace,
+                    ws_bytes, stream);
+}
+
+int qsa_sparse_gqa_prefill_fp8(const qsa_dims* dims, int32_t total_q, const uint16_t* q,
+                               const int32_t* q_req, const uint8_t* k_pool, const uint8_t* v_pool,
+                               float k_scale, float v_scale, const int32_t* page_table,
+                               int32_t pt_stride, const int32_t* sel_pos, const int32_t* sel_count,
+                               int32_t sel_stride, uint16_t* out, float* lse, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  if (total_q > 0 && !q_req) return QSA_E_NULL;
+  return gqa_common(dims, total_q, q, q_req, k_pool, v_pool, true, k_scale, v_scale, page_table,
+                    pt_stride, sel_pos, sel_count, sel_stride, nullptr, 0, out, lse, workspace,
+                    ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -21,6 +21,14 @@
 // Softmax is online (running max and sum per head, log2 domain).  The 4 waves
 // merge through LDS; with several splits, a combine kernel merges the split
 // partials.
+//
+// FP8 K/V [ailone.io model page on Qwen3.8-Flash-Next, comparison of vLLM builds:
+// a K/V cache in FP8]: the pools hold OCP E4M3 codes with one scale per pool.  The
+// rows are loaded as codes (half the bytes and registers) and turned into bf16
+// fragments just before use by v_cvt_scalef32_pk_bf16_fp8 with scale 1, which is
+// exact (every E4M3 value is a bf16 value).  k_scale is folded into the softmax
+// scale and v_scale into the output.  The K dims are permuted so that a lane reads
+// 16 contiguous bytes per row; the query fragments follow the same permutation.
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
@@ -48,31 +56,111 @@ struct KV {
   uint32_t okmask;
 };
 
-__device__ __forceinline__ void load_kv(KV& x, const int32_t* s_slot, int cb, int end_local,
-                                        const uint16_t* __restrict__ k_pool,
-                                        const uint16_t* __restrict__ v_pool, int g, int r, int j) {
-  // slot -1 = no position; its loads read slot 0 and are discarded
+// The same step as FP8 codes: K fragment pairs (16 codes = 2 fragments) and V rows
+// of 8 codes.
+struct KV8 {
+  u32x4_t k0[4], k1[4];
+  u32x2_t v[2][8];
+  uint32_t okmask;
+};
+
+template <bool kFp8> struct KVRegs { typedef KV type; };
+template <> struct KVRegs<true> { typedef KV8 type; };
+
+// Dims held by lane (r, j) in query/key fragment kc.  bf16: 32 kc + 8 j + (0..7).
+// FP8: 64 (kc/2) + 16 j + 8 (kc%2) + (0..7), so fragments 2kk and 2kk+1 of a row are
+// 16 contiguous codes.
+template <bool kFp8>
+__device__ __forceinline__ int frag_dim(int kc, int j) {
+  return kFp8 ? 64 * (kc >> 1) + 16 * j + 8 * (kc & 1) : 32 * kc + 8 * j;
+}
+
+// ok bit e: V row e of the lane is a real position; slot -1 = no position, whose
+// loads read slot 0 and are discarded
+__device__ __forceinline__ void step_slots(const int32_t* s_slot, int cb, int end_local, int r,
+                                           int j, int& s0, int& s1, int (&sv)[8],
+                                           uint32_t& ok) {
   const int li0 = cb + r, li1 = cb + 16 + r;
-  const int s0 = li0 < end_local ? s_slot[li0] : -1;
-  const int s1 = li1 < end_local ? s_slot[li1] : -1;
-  const uint16_t* k0 = k_pool + ((size_t)max(s0, 0) * kKVHeads + g) * kHeadDim + 8 * j;
-  const uint16_t* k1 = k_pool + ((size_t)max(s1, 0) * kKVHeads + g) * kHeadDim + 8 * j;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    x.k0[k] = ld16(k0 + 32 * k);
-    x.k1[k] = ld16(k1 + 32 * k);
-  }
-  uint32_t ok = 0;
+  s0 = li0 < end_local ? s_slot[li0] : -1;
+  s1 = li1 < end_local ? s_slot[li1] : -1;
+  ok = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int li = cb + (e < 4 ? 0 : 16) + 4 * j + (e & 3);
-    const int sl = li < end_local ? s_slot[li] : -1;
-    ok |= (sl >= 0 ? 1u : 0u) << e;
-    const uint16_t* vp = v_pool + ((size_t)max(sl, 0) * kKVHeads + g) * kHeadDim + 8 * r;
+    sv[e] = li < end_local ? s_slot[li] : -1;
+    ok |= (sv[e] >= 0 ? 1u : 0u) << e;
+  }
+}
+
+__device__ __forceinline__ void load_kv(KV& x, const int32_t* s_slot, int cb, int end_local,
+                                        const void* k_pool_v, const void* v_pool_v, int g, int r,
+                                        int j) {
+  const uint16_t* __restrict__ k_pool = static_cast<const uint16_t*>(k_pool_v);
+  const uint16_t* __restrict__ v_pool = static_cast<const uint16_t*>(v_pool_v);
+  int s0, s1, sv[8];
+  step_slots(s_slot, cb, end_local, r, j, s0, s1, sv, x.okmask);
+  const uint16_t* k0 = k_pool + ((size_t)max(s0, 0) * kKVHeads + g) * kHeadDim;
+  const uint16_t* k1 = k_pool + ((size_t)max(s1, 0) * kKVHeads + g) * kHeadDim;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    x.k0[k] = ld16(k0 + frag_dim<false>(k, j));
+    x.k1[k] = ld16(k1 + frag_dim<false>(k, j));
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint16_t* vp = v_pool + ((size_t)max(sv[e], 0) * kKVHeads + g) * kHeadDim + 8 * r;
     x.v[0][e] = ld16(vp);
     x.v[1][e] = ld16(vp + 128);
   }
-  x.okmask = ok;
+}
+
+__device__ __forceinline__ void load_kv(KV8& x, const int32_t* s_slot, int cb, int end_local,
+                                        const void* k_pool_v, const void* v_pool_v, int g, int r,
+                                        int j) {
+  const uint8_t* __restrict__ k_pool = static_cast<const uint8_t*>(k_pool_v);
+  const uint8_t* __restrict__ v_pool = static_cast<const uint8_t*>(v_pool_v);
+  int s0, s1, sv[8];
+  step_slots(s_slot, cb, end_local, r, j, s0, s1, sv, x.okmask);
+  const uint8_t* k0 = k_pool + ((size_t)max(s0, 0) * kKVHeads + g) * kHeadDim;
+  const uint8_t* k1 = k_pool + ((size_t)max(s1, 0) * kKVHeads + g) * kHeadDim;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    x.k0[kk] = ld16(k0 + frag_dim<true>(2 * kk, j));
+    x.k1[kk] = ld16(k1 + frag_dim<true>(2 * kk, j));
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint8_t* vp = v_pool + ((size_t)max(sv[e], 0) * kKVHeads + g) * kHeadDim + 8 * r;
+    x.v[0][e] = *reinterpret_cast<const u32x2_t*>(vp);
+    x.v[1][e] = *reinterpret_cast<const u32x2_t*>(vp + 128);
+  }
+}
+
+// 4 E4M3 codes -> 4 bf16 (2 dwords), exact.
+__device__ __forceinline__ u32x2_t fp8x4_to_bf16(uint32_t w) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return u32x2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
+__device__ __forceinline__ u32x4_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const u32x2_t a = fp8x4_to_bf16(w0), b = fp8x4_to_bf16(w1);
+  return u32x4_t{a.x, a.y, b.x, b.y};
+}
+
+// bf16 fragments of a step, for either register layout: K fragment k of tile 0/1,
+// V row e of half gm.  FP8 codes are converted where they are used.
+__device__ __forceinline__ u32x4_t kfrag(const KV& x, int tile, int k) {
+  return tile ? x.k1[k] : x.k0[k];
+}
+__device__ __forceinline__ u32x4_t kfrag(const KV8& x, int tile, int k) {
+  const u32x4_t c = tile ? x.k1[k >> 1] : x.k0[k >> 1];
+  return (k & 1) ? fp8x8_to_bf16(c.z, c.w) : fp8x8_to_bf16(c.x, c.y);
+}
+__device__ __forceinline__ u32x4_t vrow(const KV& x, int gm, int e) { return x.v[gm][e]; }
+__device__ __forceinline__ u32x4_t vrow(const KV8& x, int gm, int e) {
+  return fp8x8_to_bf16(x.v[gm][e].x, x.v[gm][e].y);
 }
 
 struct SoftmaxState {
@@ -80,13 +168,14 @@ struct SoftmaxState {
   f32x4_t acc[2][8];
 };
 
-__device__ __forceinline__ void attend_step(SoftmaxState& st, const KV& x, const u32x4_t (&qf)[8],
+template <class KVR>
+__device__ __forceinline__ void attend_step(SoftmaxState& st, const KVR& x, const u32x4_t (&qf)[8],
                                             float scale_log2) {
   f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    s0 = mfma16(x.k0[k], qf[k], s0);
-    s1 = mfma16(x.k1[k], qf[k], s1);
+    s0 = mfma16(kfrag(x, 0, k), qf[k], s0);
+    s1 = mfma16(kfrag(x, 1, k), qf[k], s1);
   }
   float xs[8];
 #pragma unroll
@@ -127,7 +216,7 @@ __device__ __forceinline__ void attend_step(SoftmaxState& st, const KV& x, const
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const bool ok = (x.okmask >> e) & 1u;
-      v[e] = ok ? x.v[gm][e] : u32x4_t{0u, 0u, 0u, 0u};
+      v[e] = ok ? vrow(x, gm, e) : u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int tau = 0; tau < 8; ++tau) {
@@ -147,14 +236,16 @@ __device__ __forceinline__ void attend_step(SoftmaxState& st, const KV& x, const
 constexpr int kMaxSplitLen = 2176;   // >= kMaxSel + QSA_MAX_EXTRA, a multiple of 128
 constexpr int kSlotsPer = (kMaxSplitLen + kThreads - 1) / kThreads;   // list entries per thread
 
+template <bool kFp8, int kDepth>
 __global__ void __launch_bounds__(kThreads)
 attn_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ q_req,
-            const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
+            const void* __restrict__ k_pool, const void* __restrict__ v_pool,
             const int32_t* __restrict__ page_table, int pt_stride, int page_size,
             const int32_t* __restrict__ sel_pos, const int32_t* __restrict__ sel_count,
             int sel_stride, const int32_t* __restrict__ extra_pos, int n_extra, float scale_log2,
-            int splits, float* __restrict__ part, uint16_t* __restrict__ out,
+            float v_scale, int splits, float* __restrict__ part, uint16_t* __restrict__ out,
             float* __restrict__ lse) {
+  typedef typename KVRegs<kFp8>::type KVR;
   __shared__ float s_m[kWaves][kGroup];
   __shared__ float s_l[kWaves][kGroup];
   __shared__ float s_acc[kWaves][kGroup][kAccPad];
@@ -174,9 +265,10 @@ attn_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ q_req,
   // Q^T operand: head r of the group (zero for the 8 padding columns)
   u32x4_t qf[8];
   {
-    const uint16_t* qrow = q + ((size_t)t * kQHeads + g * kGroup + (r & 7)) * kHeadDim + 8 * j;
+    const uint16_t* qrow = q + ((size_t)t * kQHeads + g * kGroup + (r & 7)) * kHeadDim;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) qf[k] = (r < kGroup) ? ld16(qrow + 32 * k) : u32x4_t{0u, 0u, 0u, 0u};
+    for (int k = 0; k < 8; ++k)
+      qf[k] = (r < kGroup) ? ld16(qrow + frag_dim<kFp8>(k, j)) : u32x4_t{0u, 0u, 0u, 0u};
   }
 
   // This split's share of the position list: the list's bound (2051 + extras)
@@ -227,18 +319,22 @@ attn_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ q_req,
 #pragma unroll
     for (int tau = 0; tau < 8; ++tau) st.acc[gm][tau] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // this wave's 32-position steps: w, w + 4, ...; two steps' loads in flight
+  // this wave's 32-position steps: w, w + 4, ...; kDepth steps' loads in flight
   const int stride = kWaves * kChunk;
-  KV A, B;
-  int cb = w * kChunk;
-  if (cb < len) load_kv(A, s_slot, cb, len, k_pool, v_pool, g, r, j);
-  if (cb + stride < len) load_kv(B, s_slot, cb + stride, len, k_pool, v_pool, g, r, j);
-  for (; cb < len; cb += 2 * stride) {
-    attend_step(st, A, qf, scale_log2);
-    if (cb + 2 * stride < len) load_kv(A, s_slot, cb + 2 * stride, len, k_pool, v_pool, g, r, j);
-    if (cb + stride < len) {
-      attend_step(st, B, qf, scale_log2);
-      if (cb + 3 * stride < len) load_kv(B, s_slot, cb + 3 * stride, len, k_pool, v_pool, g, r, j);
+  KVR buf[kDepth];
+  const int cb0 = w * kChunk;
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d)
+    if (cb0 + d * stride < len) load_kv(buf[d], s_slot, cb0 + d * stride, len, k_pool, v_pool, g, r, j);
+  for (int cb = cb0; cb < len; cb += kDepth * stride) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const int c = cb + d * stride;
+      if (c < len) {
+        attend_step(st, buf[d], qf, scale_log2);
+        if (c + kDepth * stride < len)
+          load_kv(buf[d], s_slot, c + kDepth * stride, len, k_pool, v_pool, g, r, j);
+      }
     }
   }
   const float m_run = st.m, l_run = st.l;
@@ -277,7 +373,7 @@ attn_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ q_req,
   }
 
   if (splits == 1) {
-    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const float inv = L > 0.f ? (kFp8 ? v_scale : 1.f) / L : 0.f;
     uint16_t* orow = out + ((size_t)t * kQHeads + g * kGroup + h) * kHeadDim + d0;
     u32x4_t ov = {pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
                   pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv)};
@@ -301,7 +397,7 @@ attn_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ q_req,
 constexpr int kMaxCombine = 8;         // splits merged from registers; more loop over memory
 
 __global__ void __launch_bounds__(256)
-combine_kernel(const float* __restrict__ part, int splits, uint16_t* __restrict__ out,
+combine_kernel(const float* __restrict__ part, int splits, float v_scale, uint16_t* __restrict__ out,
                float* __restrict__ lse) {
   const int tg = blockIdx.x;
   const int g = tg % kKVHeads;
@@ -350,7 +446,7 @@ combine_kernel(const float* __restrict__ part, int splits, uint16_t* __restrict_
     }
     M = Mn;
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const float inv = L > 0.f ? v_scale / L : 0.f;   // v_scale is 1 for bf16 pools
   uint16_t* orow = out + ((size_t)t * kQHeads + g * kGroup + h) * kHeadDim + d0;
   u32x4_t ov = {pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
                 pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv)};
@@ -378,14 +474,25 @@ size_t attn_workspace_bytes(int total_q, int n_extra) {
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
-  const float scale_log2 = a.sm_scale * kLog2e;
+  // FP8 codes stand for code * scale: k_scale goes into the logits' scale, v_scale
+  // onto the normalised output
+  const float scale_log2 = a.sm_scale * (a.fp8 ? a.k_scale : 1.f) * kLog2e;
+  const float v_scale = a.fp8 ? a.v_scale : 1.f;
   const int nblk = a.total_q * kKVHeads * a.splits;
-  hipLaunchKernelGGL(attn_kernel, dim3(nblk), dim3(kThreads), 0, stream, a.q, a.q_req, a.k_pool,
+  // Steps in flight per wave.  Split lists (decode: every CU holds one work group)
+  // run fastest with one: more only lengthens the gathers' queues in the memory
+  // system (decode FP8 22.0 / 22.5 / 24.2 / 25.7 us and bf16 30.7 / 32.0 us for
+  // depth 1 / 2 / 3 / 4).  Whole lists (prefill, many work groups per CU) gain a
+  // little from two (2160 against 2198 us).
+  auto kern = a.fp8 ? (a.splits > 1 ? attn_kernel<true, 1> : attn_kernel<true, 2>)
+                    : (a.splits > 1 ? attn_kernel<false, 1> : attn_kernel<false, 2>);
+  hipLaunchKernelGGL(kern, dim3(nblk), dim3(kThreads), 0, stream, a.q, a.q_req, a.k_pool,
                      a.v_pool, a.page_table, a.pt_stride, a.page_size, a.sel_pos, a.sel_count,
-                     a.sel_stride, a.extra_pos, a.n_extra, scale_log2, a.splits, a.part, a.out, a.lse);
+                     a.sel_stride, a.extra_pos, a.n_extra, scale_log2, v_scale, a.splits, a.part,
+                     a.out, a.lse);
   if (a.splits > 1) {
     hipLaunchKernelGGL(combine_kernel, dim3(a.total_q * kKVHeads), dim3(256), 0, stream, a.part,
-                       a.splits, a.out, a.lse);
+                       a.splits, v_scale, a.out, a.lse);
   }
   return hipGetLastError();
 }

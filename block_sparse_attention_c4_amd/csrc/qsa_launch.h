@@ -54,8 +54,10 @@ struct AttnArgs {
   float sm_scale;
   const uint16_t* q;
   const int32_t* q_req;      // NULL: query t reads request t
-  const uint16_t* k_pool;
-  const uint16_t* v_pool;
+  const void* k_pool;         // bf16, or FP8 E4M3 codes when fp8
+  const void* v_pool;
+  bool fp8;
+  float k_scale, v_scale;     // FP8 pools: a code stands for e4m3(code) * scale
   const int32_t* page_table;
   const int32_t* sel_pos;
   const int32_t* sel_count;

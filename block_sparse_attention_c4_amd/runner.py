@@ -27,17 +27,24 @@ def _i32(a, dev) -> torch.Tensor:
 class DeviceWorkload:
     """A workload resident in HBM plus its output and scratch buffers."""
 
-    def __init__(self, wl: Workload, device: str = "cuda:0", upload_pools: bool = True):
+    def __init__(self, wl: Workload, device: str = "cuda:0", upload_pools: bool = True,
+                 kv: str = "bf16"):
+        """kv = "fp8": attention reads the workload's FP8 E4M3 pools (the bf16 pools are
+        not uploaded)."""
         dev = torch.device(device)
         self.dev = dev
         self.wl = wl
+        self.kv = kv
         self.dims = B.default_dims(wl.page_size, wl.rope_theta)
         self.batch = wl.batch
         self.T = wl.total_q
         self.page_table = _i32(np.maximum(wl.page_table, 0), dev)
         self.pt_stride = int(wl.page_table.shape[1])
         nslots = wl.num_pages * wl.page_size
-        if upload_pools:
+        if upload_pools and kv == "fp8":
+            self.k_pool = torch.from_numpy(np.ascontiguousarray(wl.k_pool_fp8)).to(dev)
+            self.v_pool = torch.from_numpy(np.ascontiguousarray(wl.v_pool_fp8)).to(dev)
+        elif upload_pools:
             self.k_pool = _u16(wl.k_pool, dev)
             self.v_pool = _u16(wl.v_pool, dev)
         self.comp = torch.zeros((nslots // 4, 128), dtype=torch.int16, device=dev)
@@ -101,7 +108,18 @@ class DeviceWorkload:
 
     def attend(self, stream=None, q=None, extra=None, n_extra: int = 0) -> None:
         q = self.q if q is None else q
-        if self.wl.kind == "prefill":
+        if self.kv == "fp8" and self.wl.kind == "prefill":
+            B.qsa_sparse_gqa_prefill_fp8(self.dims, self.T, q, self.q_req, self.k_pool, self.v_pool,
+                                         self.wl.k_scale, self.wl.v_scale, self.page_table,
+                                         self.pt_stride, self.sel_pos, self.sel_count, SEL_STRIDE,
+                                         self.out, self.lse, self.ws_attn, self.ws_attn_bytes, stream)
+        elif self.kv == "fp8":
+            B.qsa_sparse_gqa_decode_fp8(self.dims, self.batch, q, self.k_pool, self.v_pool,
+                                        self.wl.k_scale, self.wl.v_scale, self.page_table,
+                                        self.pt_stride, self.sel_pos, self.sel_count, SEL_STRIDE,
+                                        extra, n_extra, self.out, self.lse, self.ws_attn,
+                                        self.ws_attn_bytes, stream)
+        elif self.wl.kind == "prefill":
             B.qsa_sparse_gqa_prefill(self.dims, self.T, q, self.q_req, self.k_pool, self.v_pool,
                                      self.page_table, self.pt_stride, self.sel_pos, self.sel_count,
                                      SEL_STRIDE, self.out, self.lse, self.ws_attn, self.ws_attn_bytes,

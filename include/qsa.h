@@ -193,6 +193,38 @@ int qsa_sparse_gqa_prefill(const qsa_dims* dims, int32_t total_q, const uint16_t
                            const int32_t* sel_count, int32_t sel_stride, uint16_t* out,
                            float* lse, void* workspace, size_t ws_bytes, void* stream);
 
+/* Stage 3 with an FP8 K/V cache - sparse GQA as qsa_sparse_gqa_decode /
+ * qsa_sparse_gqa_prefill, over pools of OCP FP8 E4M3 codes with one scale per
+ * pool.  [ailone.io model page on Qwen3.8-Flash-Next, comparison of vLLM builds: a
+ * K/V cache in FP8 runs at the speed of BF16 and holds a larger token pool.  The
+ * page states neither the FP8 format nor the scaling; E4M3 with per-pool scales is
+ * the reading implemented.]
+ *
+ * A code c of k_pool stands for the value e4m3(c) * k_scale, a code of v_pool for
+ * e4m3(c) * v_scale, where e4m3(c) = (-1)^s (1 + m/8) 2^(e-7) for exponent e > 0
+ * and (-1)^s (m/8) 2^-6 for e = 0 (bias 7, 3 mantissa bits, no infinities; the
+ * codes 0x7f and 0xff are NaN and must not appear at attended positions).  With
+ * those values the results are defined as for the bf16 calls.
+ *
+ *   k_pool, v_pool [slots, Hkv, D] uint8 codes, 16-byte aligned (half the bytes of
+ *                  the bf16 pools, same slot layout)
+ *   k_scale, v_scale (host) finite and > 0, else QSA_E_SHAPE
+ *   every other argument, the workspace included, as for the bf16 call
+ */
+int qsa_sparse_gqa_decode_fp8(const qsa_dims* dims, int32_t batch, const uint16_t* q,
+                              const uint8_t* k_pool, const uint8_t* v_pool, float k_scale,
+                              float v_scale, const int32_t* page_table, int32_t pt_stride,
+                              const int32_t* sel_pos, const int32_t* sel_count, int32_t sel_stride,
+                              const int32_t* extra_pos, int32_t n_extra, uint16_t* out, float* lse,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+int qsa_sparse_gqa_prefill_fp8(const qsa_dims* dims, int32_t total_q, const uint16_t* q,
+                               const int32_t* q_req, const uint8_t* k_pool, const uint8_t* v_pool,
+                               float k_scale, float v_scale, const int32_t* page_table,
+                               int32_t pt_stride, const int32_t* sel_pos, const int32_t* sel_count,
+                               int32_t sel_stride, uint16_t* out, float* lse, void* workspace,
+                               size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -86,9 +86,16 @@ def small(name):
     return _CACHE[key]
 
 
-def _device(wl):
-    P.log(f"[upload] {wl.name} B={wl.batch} T={wl.total_q} pages={wl.num_pages}")
-    return runner.DeviceWorkload(wl, _gpu())
+def _device(wl, kv="bf16"):
+    P.log(f"[upload] {wl.name} B={wl.batch} T={wl.total_q} pages={wl.num_pages} kv={kv}")
+    return runner.DeviceWorkload(wl, _gpu(), kv=kv)
+
+
+def fp8(wl):
+    """The workload with FP8 E4M3 copies of its K/V pools (made once)."""
+    if wl.k_pool_fp8 is None:
+        synth.with_fp8_kv(wl)
+    return wl
 
 
 def _rows(wl, sample):
@@ -240,10 +247,10 @@ def _upload_oracle_positions(dw, res, rows):
     dw.sel_count.copy_(torch.from_numpy(sc))
 
 
-def _check_attention_stage(wl, sample=None):
-    dw = _device(wl)
+def _check_attention_stage(wl, sample=None, kv="bf16"):
+    dw = _device(wl, kv)
     rows = _rows(wl, sample)
-    res = O.run_queries(wl, rows)
+    res = O.run_queries(wl, rows, kv=kv)
     _upload_oracle_positions(dw, res, range(wl.total_q) if sample is None else rows)
     dw.attend()
     torch.cuda.synchronize()
@@ -253,7 +260,7 @@ def _check_attention_stage(wl, sample=None):
     for t in rows:
         mx, _, _ = P.check_attention(out[t], lse[t], res[t], f"{wl.name} row {t}")
         worst = max(worst, mx)
-    P.log(f"[attn] {wl.name}: {len(rows)} rows, worst max-abs {worst:.2e}")
+    P.log(f"[attn] {wl.name} {kv}: {len(rows)} rows, worst max-abs {worst:.2e}")
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -267,17 +274,33 @@ def test_attention_stage_full(name):
     _check_attention_stage(wl, sample=48 if wl.kind == "prefill" else None)
 
 
+# FP8 E4M3 K/V pools with per-pool scales: the same bar, against the oracle on the
+# decoded and scaled codes
+FP8_SMALL = ["decode_ragged", "decode_page16", "prefill_ragged", "decode_batch70", "verify_chunk3"]
+
+
+@pytest.mark.parametrize("name", FP8_SMALL)
+def test_attention_stage_fp8_small(name):
+    _check_attention_stage(fp8(small(name)), kv="fp8")
+
+
+@pytest.mark.parametrize("name", ["decode_b32_loguniform_4k_128k", "prefill_chunk4096_prefix126976"])
+def test_attention_stage_fp8_full(name):
+    wl = fp8(full(name))
+    _check_attention_stage(wl, sample=48 if wl.kind == "prefill" else None, kv="fp8")
+
+
 # ------------------------------------------------------------------ end to end
 
-def _check_e2e(wl, sample=None):
-    dw = _device(wl)
+def _check_e2e(wl, sample=None, kv="bf16"):
+    dw = _device(wl, kv)
     dw.build_prefix()
     dw.step()
     torch.cuda.synchronize()
     states = P.oracle_index_states(wl)
     P.check_comp_cache(wl, dw.comp_numpy(), states)
     rows = _rows(wl, sample)
-    res = O.run_queries(wl, rows)
+    res = O.run_queries(wl, rows, kv=kv)
     gb = dw.sel_blocks.cpu().numpy()
     gp = dw.sel_pos.cpu().numpy()
     gc = dw.sel_count.cpu().numpy()
@@ -308,6 +331,10 @@ def test_end_to_end_full(name):
     _check_e2e(wl, sample=48 if wl.kind == "prefill" else None)
 
 
+def test_end_to_end_fp8_decode_full():
+    _check_e2e(fp8(full("decode_b32_loguniform_4k_128k")), kv="fp8")
+
+
 def test_planted_hot_blocks_selected_on_gpu():
     wl = full("decode_b8_l32k")
     dw = _device(wl)
@@ -321,13 +348,13 @@ def test_planted_hot_blocks_selected_on_gpu():
 
 # ------------------------------------------------------------------ IndexShare
 
-def _check_indexshare(wl):
-    dw = _device(wl)
+def _check_indexshare(wl, kv="bf16"):
+    dw = _device(wl, kv)
     dw.build_prefix()
     dw.step()                     # capture: the indexer runs on the last accepted token
     torch.cuda.synchronize()
-    cap = O.run_queries(wl)
-    res = O.run_indexshare(wl, cap)
+    cap = O.run_queries(wl, kv=kv)
+    res = O.run_indexshare(wl, cap, kv=kv)
     gb = dw.sel_blocks.cpu().numpy()
     # reuse steps over the oracle's captured selection (stage isolated)
     _upload_oracle_positions(dw, cap, range(wl.batch))
@@ -350,6 +377,10 @@ def test_indexshare_small():
 
 def test_indexshare_full():
     _check_indexshare(full("indexshare_b4_l262140"))
+
+
+def test_indexshare_fp8_small():
+    _check_indexshare(fp8(small("indexshare_small")), kv="fp8")
 
 
 # ------------------------------------------------------------------ edge cases
