@@ -118,6 +118,8 @@ class Workload:
     v_pool_fp8: np.ndarray | None = None             # their per-pool scales
     k_scale: float = 1.0
     v_scale: float = 1.0
+    mpos: list | None = None                         # B arrays [L_b, 3] int32: 3-D (MRoPE) positions
+    pair_axis: np.ndarray | None = None              # [64] uint8: position component of each rotary pair
 
     @property
     def batch(self) -> int:
@@ -248,6 +250,46 @@ def with_fp8_kv(wl: Workload) -> Workload:
 
     wl.k_pool_fp8, wl.k_scale = quantize(wl.k_pool)
     wl.v_pool_fp8, wl.v_scale = quantize(wl.v_pool)
+    return wl
+
+
+def contiguous_pair_axis(sections=(16, 24, 24)) -> np.ndarray:
+    """Axis map of contiguous MRoPE sections: the first sections[0] rotary pairs take
+    the temporal component, the next sections[1] the height, the rest the width."""
+    return np.repeat(np.arange(3), sections).astype(np.uint8)
+
+
+def mrope_positions(length: int, images) -> np.ndarray:
+    """3-D positions [length, 3] of a token stream with vision spans.
+
+    images: (start, T, H, W) tuples, sorted, non-overlapping: T*H*W vision tokens
+    from sequence index `start`.  A text token has (p, p, p), p counting on from the
+    previous token; a vision token k of a span whose first position is p0 has
+    (p0 + k // (H*W), p0 + (k // W) % H, p0 + k % W); text after a span resumes at
+    p0 + max(T, H, W)."""
+    pos = np.zeros((length, 3), dtype=np.int32)
+    nxt, t = 0, 0
+    for start, T, H, W in list(images) + [(length, 0, 0, 0)]:
+        while t < min(start, length):
+            pos[t] = nxt
+            nxt += 1
+            t += 1
+        n = min(T * H * W, length - t)
+        if n <= 0:
+            continue
+        k = np.arange(n)
+        pos[t:t + n, 0] = nxt + k // (H * W)
+        pos[t:t + n, 1] = nxt + (k // W) % H
+        pos[t:t + n, 2] = nxt + k % W
+        t += n
+        nxt += max(T, H, W)
+    return pos
+
+
+def with_mrope(wl: Workload, images_per_request, pair_axis=None) -> Workload:
+    """Give every request of wl 3-D positions with the listed vision spans."""
+    wl.mpos = [mrope_positions(int(L), imgs) for L, imgs in zip(wl.lengths, images_per_request)]
+    wl.pair_axis = contiguous_pair_axis() if pair_axis is None else np.asarray(pair_axis, np.uint8)
     return wl
 
 

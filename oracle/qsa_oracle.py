@@ -37,8 +37,16 @@ Readings where the pages are silent or garbled (each is listed in the design doc):
       mantissa bits, no infinities, S.1111.111 is NaN, largest finite 448) with one
       scale per pool; a stored code c stands for e4m3(c) * k_scale (K) or
       e4m3(c) * v_scale (V).  Attention is then as in R7 on those values.
+  R10 MRoPE [QSA: the block is turned with "the first token's MRoPE position", and
+      the indexer reuses the attention layers' MRoPE]: a token has a 3-D position
+      (temporal, height, width); each rotary pair i takes the angle
+      pos[axis(i)] * theta**(-2i/128) from one component, chosen by a per-pair axis
+      map.  The pages give no sections; the default map is contiguous sections of
+      16, 24 and 24 pairs (t, h, w).  A text token at sequence position p has the
+      position (p, p, p), which reduces MRoPE to R3.
   parity unpinned: fidelity to the real model's readings R1, R3 (pairing, rotary
-  fraction, theta) and R2's epsilon cannot be checked against the pages.
+      fraction, theta), R10's sections and R2's epsilon cannot be checked against
+      the pages.
 """
 
 from __future__ import annotations
@@ -112,13 +120,29 @@ def comp_slot(page_row, c, page_size: int):
 
 # ---------------------------------------------------------------- stage 1: keys
 
+def inv_freqs(d: int, theta: float) -> np.ndarray:
+    """theta**(-2i/d) for the d/2 rotary pairs (i, i + d/2)."""
+    return theta ** (-(2.0 * np.arange(d // 2)) / d)
+
+
 def rotate(x, pos, theta: float) -> np.ndarray:
     """Rotary phase of position `pos` on the last axis of x (reading R3)."""
     x = np.asarray(x, dtype=np.float64)
-    d = x.shape[-1]
-    half = d // 2
-    inv_freq = theta ** (-(2.0 * np.arange(half)) / d)
-    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv_freq
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv_freqs(x.shape[-1], theta)
+    return rotate_by(x, ang)
+
+
+def mrope_angles(pos3, pair_axis, theta: float, d: int = 128) -> np.ndarray:
+    """Angles of MRoPE (reading R10): pair i of a token at 3-D position pos3 turns
+    by pos3[axis(i)] * theta**(-2i/d).  pos3: [..., 3] -> [..., d/2]."""
+    pos3 = np.asarray(pos3, dtype=np.float64)
+    return pos3[..., np.asarray(pair_axis, dtype=np.int64)] * inv_freqs(d, theta)
+
+
+def rotate_by(x, ang) -> np.ndarray:
+    """Turn pair (i, i + d/2) of the last axis of x by ang[..., i] (rotate-half)."""
+    x = np.asarray(x, dtype=np.float64)
+    half = x.shape[-1] // 2
     c, s = np.cos(ang), np.sin(ang)
     a, b = x[..., :half], x[..., half:]
     return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
@@ -143,23 +167,39 @@ def compress_blocks(raw_bits, first_pos, theta: float) -> np.ndarray:
 
     raw_bits: [n, 4, d] bf16 bits; first_pos: [n] -> [n, d] bf16 bits.
     """
+    return f64_to_bf16_bits(rotate(normalised_means(raw_bits), first_pos, theta))
+
+
+def compress_blocks_mrope(raw_bits, first_pos3, pair_axis, theta: float) -> np.ndarray:
+    """compress_blocks with MRoPE (R10): each block is turned by the angles of its
+    first token's 3-D position.  first_pos3: [n, 3]."""
+    k = normalised_means(raw_bits)
+    return f64_to_bf16_bits(rotate_by(k, mrope_angles(first_pos3, pair_axis, theta, k.shape[-1])))
+
+
+def normalised_means(raw_bits) -> np.ndarray:
+    """FP32 block means (R4), L2-normalised in float64 with the floor of R2."""
     m = block_mean_fp32(raw_bits).astype(np.float64)
     norm = np.sqrt(np.sum(m * m, axis=-1, keepdims=True))
-    kbar = m / np.maximum(norm, NORM_FLOOR)
-    return f64_to_bf16_bits(rotate(kbar, first_pos, theta))
+    return m / np.maximum(norm, NORM_FLOOR)
 
 
-def build_index_state(raw_bits, length: int, theta: float):
+def build_index_state(raw_bits, length: int, theta: float, mpos=None, pair_axis=None):
     """Index state of a request after tokens 0..length-1 are ingested [QSA]:
     one compressed key per complete block, and the raw keys of the unfinished
-    block's tokens in ring slots t % 4.
+    block's tokens in ring slots t % 4.  With mpos ([length, 3] 3-D positions) the
+    blocks are turned by MRoPE (R10) with the axis map pair_axis.
 
     Returns (comp [length//4, d] bf16 bits, ring dict {slot: bits [d]}).
     """
     raw = np.asarray(raw_bits)[:length]
     n_c = length // BLOCK
-    comp = compress_blocks(raw[:BLOCK * n_c].reshape(n_c, BLOCK, raw.shape[-1]),
-                           BLOCK * np.arange(n_c), theta)
+    blocks = raw[:BLOCK * n_c].reshape(n_c, BLOCK, raw.shape[-1])
+    if mpos is None:
+        comp = compress_blocks(blocks, BLOCK * np.arange(n_c), theta)
+    else:
+        first = np.asarray(mpos)[:BLOCK * n_c:BLOCK]
+        comp = compress_blocks_mrope(blocks, first, pair_axis, theta)
     ring = {t % BLOCK: raw[t].copy() for t in range(BLOCK * n_c, length)}
     return comp, ring
 
@@ -290,7 +330,10 @@ def indexshare_step(captured_positions, p_cap: int, j: int, q_bits, page_row, k_
 # v_pool_fp8, k_scale, v_scale).
 
 def index_state(wl, b: int, length: int):
-    return build_index_state(wl.raw_idx_k[b], length, wl.rope_theta)
+    mpos = getattr(wl, "mpos", None)
+    if mpos is None:
+        return build_index_state(wl.raw_idx_k[b], length, wl.rope_theta)
+    return build_index_state(wl.raw_idx_k[b], length, wl.rope_theta, mpos[b], wl.pair_axis)
 
 
 def comp_cache_entries(wl, b: int, comp_bits):

@@ -308,6 +308,53 @@ def test_gqa_matches_torch_sdpa():
     np.testing.assert_allclose(out, ref, atol=1e-12)
 
 
+# ------------------------------------------------------------------ MRoPE (reading R10)
+
+def test_mrope_text_positions_reduce_to_1d_rope():
+    rng = np.random.default_rng(17)
+    raw = bits(rng.standard_normal((203, 128)))
+    pos3 = np.repeat(np.arange(203)[:, None], 3, axis=1)
+    for axis in (synth.contiguous_pair_axis(), np.arange(64) % 3):
+        comp3, ring3 = O.build_index_state(raw, 203, 1e7, pos3, axis)
+        comp1, ring1 = O.build_index_state(raw, 203, 1e7)
+        np.testing.assert_array_equal(comp3, comp1)
+        assert ring3.keys() == ring1.keys()
+
+
+def _one_block_with_mean(dims):
+    # four equal raw keys with ones at `dims`: the mean is that vector exactly
+    raw = np.zeros((4, 128), np.float32)
+    raw[:, dims] = 1.0
+    return bits(raw)[None]
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "interleaved"])
+def test_mrope_block_turned_by_each_pairs_own_axis(layout):
+    # mean e0 + e20 + e50, first token at (t, h, w) = (5, 2, 9).  Contiguous
+    # sections 16/24/24 put pairs 0, 20, 50 on t, h, w; the interleaved map i % 3 on
+    # t, w, w.  Pair i's dims (i, i + 64) become cos(a_i), sin(a_i) over sqrt(3).
+    axis = synth.contiguous_pair_axis() if layout == "contiguous" else (np.arange(64) % 3).astype(np.uint8)
+    pos = {"contiguous": {0: 5, 20: 2, 50: 9}, "interleaved": {0: 5, 20: 9, 50: 9}}[layout]
+    key = O.bf16_to_f64(O.compress_blocks_mrope(_one_block_with_mean([0, 20, 50]),
+                                                np.array([[5, 2, 9]]), axis, 1e7))[0]
+    for i, p in pos.items():
+        a = p * 1e7 ** (-2.0 * i / 128)
+        for dim, want in ((i, math.cos(a) / math.sqrt(3)), (i + 64, math.sin(a) / math.sqrt(3))):
+            # within half a bf16 step of the exact value
+            assert abs(key[dim] - want) <= 2.0 ** (math.floor(math.log2(abs(want))) - 8), (dim, key[dim], want)
+    others = np.setdiff1d(np.arange(128), [0, 20, 50, 64, 84, 114])
+    assert np.all(key[others] == 0.0)
+
+
+def test_mrope_positions_of_a_vision_span():
+    # text 0..2, a 1 x 2 x 3 image from index 3, text again from position 3 + 3
+    pos = synth.mrope_positions(11, [(3, 1, 2, 3)])
+    want = [(0, 0, 0), (1, 1, 1), (2, 2, 2),
+            (3, 3, 3), (3, 3, 4), (3, 3, 5), (3, 4, 3), (3, 4, 4), (3, 4, 5),
+            (6, 6, 6), (7, 7, 7)]
+    assert [tuple(r) for r in pos] == want
+
+
 # ------------------------------------------------------------------ FP8 K/V (reading R9)
 
 def test_e4m3_decode_hand_values():
