@@ -13,6 +13,7 @@ pages.  --workload picks one of the other seeded workloads instead:
   verify_b32x4_loguniform_4k_128k      target verification: 4 query tokens per request
                                        (capture token + 3 drafts), batch 32, seed 1006
   decode_b32_loguniform_4k_128k_fp8kv  the headline decode with FP8 E4M3 K/V pools
+  prefill_chunk4096_prefix126976_mrope the prefill chunk as image tokens (MRoPE builder)
 
 A step is one pass of the whole hot path for the batch: ingest the step's indexer
 keys (builder), score + top-512 + expansion (indexer), sparse GQA.  A reuse step
@@ -64,6 +65,11 @@ WORKLOADS = {
         metric="QSA decode tokens/s at 128K ctx with an FP8 E4M3 K/V cache (indexer+top-k+sparse GQA); "
                "HBM GB/s vs peak",
         context="log-uniform 4096..131072"),
+    "prefill_chunk4096_prefix126976_mrope": dict(
+        kind="prefill", source="prefill_chunk4096_prefix126976", steps=40, warmup=5, sets=2,
+        images=[[(20000, 4, 32, 32), (126976, 1, 64, 64)]],
+        metric="QSA chunked-prefill tokens/s with MRoPE positions (the chunk is one 64 x 64 image)",
+        context="126976 cached (a 4 x 32 x 32 video span inside) + 4096 new image tokens"),
     "verify_b32x4_loguniform_4k_128k": dict(
         kind="verify", steps=1000, warmup=20, sets=4,
         metric="QSA target-verify tokens/s, batch 32 x 4 query tokens, log-uniform 4K-128K ctx; "
@@ -374,6 +380,8 @@ def main() -> int:
     wl = synth.FULL_SIZE[cfg.get("source", args.workload)]()
     if kv == "fp8":
         synth.with_fp8_kv(wl)
+    if cfg.get("images"):
+        synth.with_mrope(wl, cfg["images"])
     base = runner.DeviceWorkload(wl, "cuda:0", kv=kv)
     base.build_prefix()
     torch.cuda.synchronize()
@@ -472,6 +480,9 @@ def main() -> int:
     config = {"workload": args.workload, "batch": wl.batch, "seed": wl.seed, "context": cfg["context"],
               "q_heads": 16, "kv_heads": 2, "head_dim": 256, "indexer": "4x128", "topk_blocks": 512,
               "page_size": wl.page_size, "input_sets": len(sets), "launch": launch}
+    if cfg.get("images"):
+        config["rope"] = "mrope, contiguous sections 16/24/24 of the 64 indexer pairs"
+        config["vision_spans"] = [list(map(list, spans)) for spans in cfg["images"]]
     result = {"metric": cfg["metric"], "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": steps,
               "warmup": warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
               "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": config}

@@ -34,7 +34,7 @@ QSA_MAX_EXTRA = 8
 
 EXPORTED = ["qsa_status_string", "qsa_workspace_bytes", "qsa_build_index_keys", "qsa_index_topk",
             "qsa_sparse_gqa_decode", "qsa_sparse_gqa_prefill", "qsa_sparse_gqa_decode_fp8",
-            "qsa_sparse_gqa_prefill_fp8"]
+            "qsa_sparse_gqa_prefill_fp8", "qsa_build_index_keys_mrope"]
 
 
 class QsaError(RuntimeError):
@@ -91,6 +91,9 @@ def lib() -> ctypes.CDLL:
         L.qsa_sparse_gqa_prefill_fp8.restype = ctypes.c_int
         L.qsa_sparse_gqa_prefill_fp8.argtypes = [ctypes.POINTER(QsaDims), _I, _P, _P, _P, _P, _F, _F,
                                                  _P, _I, _P, _P, _I, _P, _P, _P, _SZ, _P]
+        L.qsa_build_index_keys_mrope.restype = ctypes.c_int
+        L.qsa_build_index_keys_mrope.argtypes = [ctypes.POINTER(QsaDims), _I, _P, _P, _P, _P, _I, _I,
+                                                 _P, _I, _P, _P, _P, _P, _P]
         _lib = L
     return _lib
 
@@ -185,3 +188,16 @@ def qsa_sparse_gqa_prefill_fp8(dims, total_q, q, q_req, k_pool, v_pool, k_scale,
                                           _ptr(sel_count), sel_stride, _ptr(out), _ptr(lse),
                                           _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "qsa_sparse_gqa_prefill_fp8")
+
+
+def qsa_build_index_keys_mrope(dims, batch, new_idx_k, new_mpos, cu_new, len_before, total_new,
+                               max_new, page_table, pt_stride, pair_axis, ring, ring_mpos, comp_cache,
+                               stream=None) -> None:
+    """pair_axis: 64 host values (0 temporal, 1 height, 2 width), e.g. a numpy array."""
+    axis = (ctypes.c_uint8 * 64)(*[int(v) for v in pair_axis])
+    st = lib().qsa_build_index_keys_mrope(ctypes.byref(dims), batch, _ptr(new_idx_k), _ptr(new_mpos),
+                                          _ptr(cu_new), _ptr(len_before), total_new, max_new,
+                                          _ptr(page_table), pt_stride, ctypes.addressof(axis),
+                                          _ptr(ring), _ptr(ring_mpos), _ptr(comp_cache),
+                                          _stream(stream))
+    _check(st, "qsa_build_index_keys_mrope")

@@ -59,10 +59,39 @@ size_t qsa_workspace_bytes(const qsa_dims* dims, int op, int32_t total_q, int32_
   }
 }
 
+static int build_common(const qsa_dims* dims, int32_t batch, const uint16_t* new_idx_k,
+                        const int32_t* new_mpos, const int32_t* cu_new, const int32_t* len_before,
+                        int32_t total_new, int32_t max_new, const int32_t* page_table,
+                        int32_t pt_stride, const uint8_t* pair_axis, uint16_t* ring,
+                        int32_t* ring_mpos, uint16_t* comp_cache, void* stream);
+
 int qsa_build_index_keys(const qsa_dims* dims, int32_t batch, const uint16_t* new_idx_k,
                          const int32_t* cu_new, const int32_t* len_before, int32_t total_new,
                          int32_t max_new, const int32_t* page_table, int32_t pt_stride,
                          uint16_t* ring, uint16_t* comp_cache, void* stream) {
+  return build_common(dims, batch, new_idx_k, nullptr, cu_new, len_before, total_new, max_new,
+                      page_table, pt_stride, nullptr, ring, nullptr, comp_cache, stream);
+}
+
+int qsa_build_index_keys_mrope(const qsa_dims* dims, int32_t batch, const uint16_t* new_idx_k,
+                               const int32_t* new_mpos, const int32_t* cu_new,
+                               const int32_t* len_before, int32_t total_new, int32_t max_new,
+                               const int32_t* page_table, int32_t pt_stride,
+                               const uint8_t* pair_axis, uint16_t* ring, int32_t* ring_mpos,
+                               uint16_t* comp_cache, void* stream) {
+  if (!pair_axis) return QSA_E_NULL;
+  for (int i = 0; i < 64; ++i)
+    if (pair_axis[i] > 2) return QSA_E_SHAPE;
+  if (batch > 0 && total_new > 0 && (!new_mpos || !ring_mpos)) return QSA_E_NULL;
+  return build_common(dims, batch, new_idx_k, new_mpos, cu_new, len_before, total_new, max_new,
+                      page_table, pt_stride, pair_axis, ring, ring_mpos, comp_cache, stream);
+}
+
+static int build_common(const qsa_dims* dims, int32_t batch, const uint16_t* new_idx_k,
+                        const int32_t* new_mpos, const int32_t* cu_new, const int32_t* len_before,
+                        int32_t total_new, int32_t max_new, const int32_t* page_table,
+                        int32_t pt_stride, const uint8_t* pair_axis, uint16_t* ring,
+                        int32_t* ring_mpos, uint16_t* comp_cache, void* stream) {
   int st = check_dims(dims);
   if (st != QSA_OK) return st;
   if (batch < 0 || total_new < 0 || max_new < 0 || max_new > total_new || pt_stride < 1 ||
@@ -83,6 +112,9 @@ int qsa_build_index_keys(const qsa_dims* dims, int32_t batch, const uint16_t* ne
   a.page_table = page_table;
   a.ring = ring;
   a.comp = comp_cache;
+  a.new_mpos = new_mpos;
+  a.ring_mpos = ring_mpos;
+  a.pair_axis = pair_axis;
   return hip_status(qsa::launch_build(a, static_cast<hipStream_t>(stream)));
 }
 

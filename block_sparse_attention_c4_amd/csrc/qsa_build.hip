@@ -14,6 +14,12 @@
 // position 262140 (an FP32 angle would be off by up to ~0.016 rad there).  The
 // inverse frequencies theta^(-2i/128) come from the host's libm; the angle is
 // reduced to [-pi, pi] with a two-constant Cody-Waite step before sincos.
+//
+// MRoPE [same section: the block is turned with the first token's MRoPE position;
+// the indexer reuses the attention layers' MRoPE]: with 3-D token positions
+// (temporal, height, width), pair i turns by pos[axis(i)] * theta^(-2i/128), the
+// per-pair axis map coming from the host.  The positions of the unfinished
+// block's tokens wait in a position ring beside the key ring.
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
@@ -32,7 +38,8 @@ __global__ void __launch_bounds__(64)
 build_kernel(const uint16_t* __restrict__ new_k, const int32_t* __restrict__ cu_new,
              const int32_t* __restrict__ len_before, const int32_t* __restrict__ page_table,
              int pt_stride, int page_size, uint16_t* __restrict__ ring,
-             uint16_t* __restrict__ comp, RopeTable rope) {
+             uint16_t* __restrict__ comp, const int32_t* __restrict__ new_mpos,
+             int32_t* __restrict__ ring_mpos, RopeTable rope) {
   const int b = blockIdx.y;
   const int off = cu_new[b];
   const int n = cu_new[b + 1] - off;
@@ -66,6 +73,15 @@ build_kernel(const uint16_t* __restrict__ new_k, const int32_t* __restrict__ cu_
 #pragma unroll
     for (int e = 0; e < 8; ++e) m[e] = m[e] * 0.25f;
   }
+  // 3-D position of the block's first token (slot 0 of the ring when it is older
+  // than this call)
+  int p3[3] = {0, 0, 0};
+  if (complete && new_mpos) {
+    const int t = kBlock * c;
+    const int32_t* src = (t < lb) ? ring_mpos + (size_t)b * kBlock * 3 : new_mpos + (size_t)(off + t - lb) * 3;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) p3[k] = src[k];
+  }
   // Every ring read of this launch happens above, in work group 0 (only block
   // c0 can hold tokens older than this call).  Work group 0 writes the ring
   // only after its reads.
@@ -76,6 +92,9 @@ build_kernel(const uint16_t* __restrict__ new_k, const int32_t* __restrict__ cu_
       const uint32_t* src = reinterpret_cast<const uint32_t*>(new_k + (size_t)(off + t - lb) * kIdxDim);
       uint32_t* dst = reinterpret_cast<uint32_t*>(ring + ((size_t)b * kBlock + (t & 3)) * kIdxDim);
       dst[threadIdx.x] = src[threadIdx.x];   // 64 lanes x 2 bf16 = 128 dims
+      if (new_mpos && threadIdx.x < 3)
+        ring_mpos[((size_t)b * kBlock + (t & 3)) * 3 + threadIdx.x] =
+            new_mpos[(size_t)(off + t - lb) * 3 + threadIdx.x];
     }
   }
   if (!complete) return;
@@ -97,7 +116,7 @@ build_kernel(const uint16_t* __restrict__ new_k, const int32_t* __restrict__ cu_
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int i = 4 * j + e;
-    const double x = pos * rope.inv_freq[i];
+    const double x = (new_mpos ? (double)p3[rope.axis[i]] : pos) * rope.inv_freq[i];
     const double k = rint(x * kInvTwoPi);
     double red = fma(-k, kTwoPiHi, x);
     red = fma(-k, kTwoPiLo, red);
@@ -124,13 +143,16 @@ build_kernel(const uint16_t* __restrict__ new_k, const int32_t* __restrict__ cu_
 
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream) {
   RopeTable rope;
-  for (int i = 0; i < kIdxDim / 2; ++i)
+  for (int i = 0; i < kIdxDim / 2; ++i) {
     rope.inv_freq[i] = std::pow((double)a.theta, -(2.0 * i) / (double)kIdxDim);
+    rope.axis[i] = a.pair_axis ? a.pair_axis[i] : 0;
+  }
   // blocks touched by n new tokens starting anywhere: at most n/4 + 2
   const int units = a.max_new / kBlock + 2;
   dim3 grid((units + kUnits - 1) / kUnits, a.batch);
   hipLaunchKernelGGL(build_kernel, grid, dim3(64), 0, stream, a.new_k, a.cu_new, a.len_before,
-                     a.page_table, a.pt_stride, a.page_size, a.ring, a.comp, rope);
+                     a.page_table, a.pt_stride, a.page_size, a.ring, a.comp, a.new_mpos,
+                     a.ring_mpos, rope);
   return hipGetLastError();
 }
 

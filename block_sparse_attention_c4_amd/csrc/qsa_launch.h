@@ -9,6 +9,7 @@ namespace qsa {
 
 struct RopeTable {
   double inv_freq[64];   // theta^(-2i/128), i < 64
+  uint8_t axis[64];      // MRoPE: position component (0 t, 1 h, 2 w) that turns pair i
 };
 
 struct BuildArgs {
@@ -20,6 +21,9 @@ struct BuildArgs {
   const int32_t* page_table;
   uint16_t* ring;
   uint16_t* comp;
+  const int32_t* new_mpos;   // [total_new, 3] 3-D positions, or NULL: 1-D RoPE at 4c
+  int32_t* ring_mpos;        // [batch, 4, 3] positions of the ring's tokens (MRoPE only)
+  const uint8_t* pair_axis;  // host [64] (MRoPE only)
 };
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
 

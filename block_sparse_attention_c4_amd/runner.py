@@ -76,6 +76,9 @@ class DeviceWorkload:
         self.step_len_before = _i32(pre, dev)
         self.step_total = int(n_new.sum())
         self.step_max = int(n_new.max())
+        if wl.mpos is not None:     # MRoPE positions: a position ring and the step's positions
+            self.ring_mpos = torch.zeros((self.batch, 4, 3), dtype=torch.int32, device=dev)
+            self.step_mpos = _i32(np.concatenate([wl.mpos[b][pre[b]:lens[b]] for b in range(self.batch)]), dev)
         if wl.kind == "indexshare":
             self.extra = torch.full((self.batch, 4), -1, dtype=torch.int32, device=dev)
             self.reuse_q = _u16(wl.reuse_q, dev)
@@ -91,11 +94,24 @@ class DeviceWorkload:
         new_k = _u16(keys, self.dev)
         cu = _i32(np.concatenate([[0], np.cumsum(pre)]), self.dev)
         lb = torch.zeros(self.batch, dtype=torch.int32, device=self.dev)
-        B.qsa_build_index_keys(self.dims, self.batch, new_k, cu, lb, int(pre.sum()), int(pre.max()),
-                               self.page_table, self.pt_stride, self.ring, self.comp, stream)
+        if wl.mpos is not None:
+            mp = _i32(np.concatenate([wl.mpos[b][:pre[b]] for b in range(self.batch)]), self.dev)
+            B.qsa_build_index_keys_mrope(self.dims, self.batch, new_k, mp, cu, lb, int(pre.sum()),
+                                         int(pre.max()), self.page_table, self.pt_stride, wl.pair_axis,
+                                         self.ring, self.ring_mpos, self.comp, stream)
+            del mp
+        else:
+            B.qsa_build_index_keys(self.dims, self.batch, new_k, cu, lb, int(pre.sum()), int(pre.max()),
+                                   self.page_table, self.pt_stride, self.ring, self.comp, stream)
         del new_k   # the caching allocator orders its reuse after the launch on this stream
 
     def build_step(self, stream=None) -> None:
+        if self.wl.mpos is not None:
+            B.qsa_build_index_keys_mrope(self.dims, self.batch, self.step_new_k, self.step_mpos,
+                                         self.step_cu, self.step_len_before, self.step_total,
+                                         self.step_max, self.page_table, self.pt_stride,
+                                         self.wl.pair_axis, self.ring, self.ring_mpos, self.comp, stream)
+            return
         B.qsa_build_index_keys(self.dims, self.batch, self.step_new_k, self.step_cu,
                                self.step_len_before, self.step_total, self.step_max, self.page_table,
                                self.pt_stride, self.ring, self.comp, stream)

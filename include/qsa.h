@@ -122,6 +122,34 @@ int qsa_build_index_keys(const qsa_dims* dims, int32_t batch, const uint16_t* ne
                          int32_t max_new, const int32_t* page_table, int32_t pt_stride,
                          uint16_t* ring, uint16_t* comp_cache, void* stream);
 
+/* Stage 1 with MRoPE positions - as qsa_build_index_keys, for models whose tokens
+ * carry 3-D rotary positions (temporal, height, width; image and video tokens).
+ * [QSA section: the block's mean is turned with the first token's MRoPE position,
+ * and the indexer reuses the attention layers' MRoPE implementation.  The pages
+ * give no section layout; the axis map is an argument.]
+ *
+ * Every step is that of qsa_build_index_keys except the angle: pair (i, i+64) of
+ * block c is turned by  P[pair_axis[i]] * theta^(-2i/128),  where P is the 3-D
+ * position of the block's first token 4c.  A text token whose position is
+ * (p, p, p) at sequence index p gives the same keys as qsa_build_index_keys.
+ *
+ *   new_mpos   [total_new, 3] int32       3-D positions of the new tokens (read)
+ *   pair_axis  [64] uint8 (host)          0 = temporal, 1 = height, 2 = width;
+ *                                         other values give QSA_E_SHAPE.  Contiguous
+ *                                         sections of 16, 24, 24 pairs are the usual
+ *                                         layout; an interleaved map is allowed too
+ *   ring_mpos  [batch, 4, 3] int32        in/out: positions of the ring's tokens,
+ *                                         slot t % 4, kept like the key ring
+ *   every other argument as for qsa_build_index_keys.  The same ring and
+ *   compressed cache may not be driven by both calls for one request.
+ */
+int qsa_build_index_keys_mrope(const qsa_dims* dims, int32_t batch, const uint16_t* new_idx_k,
+                               const int32_t* new_mpos, const int32_t* cu_new,
+                               const int32_t* len_before, int32_t total_new, int32_t max_new,
+                               const int32_t* page_table, int32_t pt_stride,
+                               const uint8_t* pair_axis, uint16_t* ring, int32_t* ring_mpos,
+                               uint16_t* comp_cache, void* stream);
+
 /* Stage 2 - indexer: score, top-512, expansion.  [QSA section: a query scores
  * the visible compressed blocks, the best 512 are kept and expanded to 2048
  * token positions, and the 0..3 tokens of the unfinished block are appended,

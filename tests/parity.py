@@ -42,7 +42,7 @@ def oracle_index_states(wl, lengths=None):
     lengths = wl.lengths if lengths is None else lengths
     out = []
     for b in range(wl.batch):
-        out.append(O.build_index_state(wl.raw_idx_k[b], int(lengths[b]), wl.rope_theta))
+        out.append(O.index_state(wl, b, int(lengths[b])))
     return out
 
 

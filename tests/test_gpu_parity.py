@@ -126,6 +126,7 @@ def _check_builder(wl):
     n, nd = P.check_comp_cache(wl, dw.comp_numpy(), states)
     P.check_ring(dw.ring_numpy(), states)
     P.log(f"[builder] {wl.name}: {n} keys, {nd} not bit-identical (<= 1 ulp)")
+    return dw
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -157,6 +158,61 @@ def test_builder_incremental_decode_matches_bulk():
     states = P.oracle_index_states(wl)
     P.check_comp_cache(wl, dw.comp_numpy(), states)
     P.check_ring(dw.ring_numpy(), states)
+
+
+# MRoPE positions: vision spans in the cached prefix, inside the step's chunk and under
+# the decode token; chunks that start inside a block read the first token's position
+# from the position ring
+MROPE = {
+    "mrope_prefill": lambda: synth.with_mrope(
+        synth.make_workload("mrope_prefill", "prefill", 317, [3000, 9000], chunk=37),
+        [[(100, 1, 16, 16), (2970, 1, 2, 8)], [(5000, 2, 8, 8)]]),
+    "mrope_decode": lambda: synth.with_mrope(
+        synth.make_workload("mrope_decode", "decode", 318, [4099, 777, 2100, 6]),
+        [[(50, 1, 32, 32)], [(700, 1, 7, 11)], [], [(1, 1, 1, 3)]]),
+    "mrope_interleaved": lambda: synth.with_mrope(
+        synth.make_workload("mrope_interleaved", "prefill", 319, [2501, 700], chunk=9),
+        [[(1000, 3, 10, 12)], [(690, 1, 3, 3)]], pair_axis=np.arange(64) % 3),
+}
+
+
+def mrope(name):
+    key = "mrope:" + name
+    if key not in _CACHE:
+        _CACHE[key] = MROPE[name]()
+    return _CACHE[key]
+
+
+@pytest.mark.parametrize("name", list(MROPE))
+def test_builder_mrope(name):
+    wl = mrope(name)
+    dw = _check_builder(wl)
+    # the position ring holds the unfinished block's tokens, slot t % 4
+    ring_pos = dw.ring_mpos.cpu().numpy()
+    for b in range(wl.batch):
+        L = int(wl.lengths[b])
+        for t in range(4 * (L // 4), L):
+            np.testing.assert_array_equal(ring_pos[b, t % 4], wl.mpos[b][t], err_msg=f"{name} {b} {t}")
+
+
+@pytest.mark.parametrize("name", list(MROPE))
+def test_end_to_end_mrope(name):
+    _check_e2e(mrope(name))
+
+
+def test_builder_mrope_text_positions_equal_1d_builder():
+    # (p, p, p) positions through the MRoPE call give the 1-D call's keys, bit for bit
+    wl = synth.make_workload("mrope_text", "prefill", 320, [5000, 2222], chunk=45)
+    dw1 = _device(wl)
+    dw1.build_prefix()
+    dw1.build_step()
+    synth.with_mrope(wl, [[], []])
+    dw3 = _device(wl)
+    dw3.build_prefix()
+    dw3.build_step()
+    torch.cuda.synchronize()
+    assert torch.equal(dw1.comp, dw3.comp)
+    assert torch.equal(dw1.ring, dw3.ring)
 
 
 # ------------------------------------------------------------------ stage 2 (fed oracle keys)
