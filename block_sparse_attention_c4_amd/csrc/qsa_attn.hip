@@ -321,19 +321,36 @@ attn_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ q_req,
 
   // this wave's 32-position steps: w, w + 4, ...; kDepth steps' loads in flight
   const int stride = kWaves * kChunk;
-  KVR buf[kDepth];
   const int cb0 = w * kChunk;
+  if constexpr (kDepth == 1) {
+    // A list that ends inside a chunk (the 0..3 tokens of the unfinished block, or
+    // drafted positions) leaves a last chunk of a few rows.  Its wave would pay one
+    // more full round trip for them, and its work group would finish last; so that
+    // chunk is requested with the wave's first chunk and attended right after it.
+    const int last = ((len + kChunk - 1) / kChunk - 1) * kChunk;
+    const bool early_tail = (len % kChunk) != 0 && last >= stride && last % stride == cb0;
+    KVR x, tail;
+    if (early_tail) load_kv(tail, s_slot, last, len, k_pool, v_pool, g, r, j);
+    const int end = early_tail ? last : len;
+    for (int cb = cb0; cb < end; cb += stride) {
+      load_kv(x, s_slot, cb, len, k_pool, v_pool, g, r, j);
+      attend_step(st, x, qf, scale_log2);
+      if (early_tail && cb == cb0) attend_step(st, tail, qf, scale_log2);
+    }
+  } else {
+    KVR buf[kDepth];
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d)
-    if (cb0 + d * stride < len) load_kv(buf[d], s_slot, cb0 + d * stride, len, k_pool, v_pool, g, r, j);
-  for (int cb = cb0; cb < len; cb += kDepth * stride) {
+    for (int d = 0; d < kDepth; ++d)
+      if (cb0 + d * stride < len) load_kv(buf[d], s_slot, cb0 + d * stride, len, k_pool, v_pool, g, r, j);
+    for (int cb = cb0; cb < len; cb += kDepth * stride) {
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-      const int c = cb + d * stride;
-      if (c < len) {
-        attend_step(st, buf[d], qf, scale_log2);
-        if (c + kDepth * stride < len)
-          load_kv(buf[d], s_slot, c + kDepth * stride, len, k_pool, v_pool, g, r, j);
+      for (int d = 0; d < kDepth; ++d) {
+        const int c = cb + d * stride;
+        if (c < len) {
+          attend_step(st, buf[d], qf, scale_log2);
+          if (c + kDepth * stride < len)
+            load_kv(buf[d], s_slot, c + kDepth * stride, len, k_pool, v_pool, g, r, j);
+        }
       }
     }
   }
