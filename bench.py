@@ -7,6 +7,7 @@ top-512 blocks, paged bf16 K/V (page 64) in one shared pool with interleaved
 pages.  --workload picks one of the other seeded workloads instead:
 
   decode_b1_l4099, decode_b8_l32k      other decode batches
+  decode_b8_l131072                    batch 8 at exactly 131072 tokens (seed 1007)
   prefill_chunk4096_prefix126976       4096 new tokens on a 126976-token prefix
   indexshare_b4_l262140                batch 4 at L = 262140: IndexShare reuse steps,
                                        with full decode steps timed beside them
@@ -14,6 +15,7 @@ pages.  --workload picks one of the other seeded workloads instead:
                                        (capture token + 3 drafts), batch 32, seed 1006
   decode_b32_loguniform_4k_128k_fp8kv  the headline decode with FP8 E4M3 K/V pools
   prefill_chunk4096_prefix126976_mrope the prefill chunk as image tokens (MRoPE builder)
+  prefill_chunk4096_prefix126976_fp8kv the prefill chunk with FP8 E4M3 K/V pools
 
 A step is one pass of the whole hot path for the batch: ingest the step's indexer
 keys (builder), score + top-512 + expansion (indexer), sparse GQA.  A reuse step
@@ -52,6 +54,9 @@ WORKLOADS = {
                            metric="QSA decode tokens/s, batch 8 at 32K ctx", context="32768 + U{0..3}"),
     "decode_b1_l4099": dict(kind="decode", steps=2000, warmup=50, sets=4,
                             metric="QSA decode tokens/s, batch 1 at 4099 ctx", context="4099"),
+    "decode_b8_l131072": dict(kind="decode", steps=2000, warmup=50, sets=4,
+                              metric="QSA decode tokens/s, batch 8 at 131072 ctx; HBM GB/s vs peak",
+                              context="131072"),
     "prefill_chunk4096_prefix126976": dict(
         kind="prefill", steps=40, warmup=5, sets=2,
         metric="QSA chunked-prefill tokens/s, 4096-token chunk on a 126976-token prefix",
@@ -65,6 +70,11 @@ WORKLOADS = {
         metric="QSA decode tokens/s at 128K ctx with an FP8 E4M3 K/V cache (indexer+top-k+sparse GQA); "
                "HBM GB/s vs peak",
         context="log-uniform 4096..131072"),
+    "prefill_chunk4096_prefix126976_fp8kv": dict(
+        kind="prefill", kv="fp8", source="prefill_chunk4096_prefix126976", steps=40, warmup=5, sets=2,
+        metric="QSA chunked-prefill tokens/s with an FP8 E4M3 K/V cache, 4096-token chunk on a "
+               "126976-token prefix",
+        context="126976 cached + 4096 new"),
     "prefill_chunk4096_prefix126976_mrope": dict(
         kind="prefill", source="prefill_chunk4096_prefix126976", steps=40, warmup=5, sets=2,
         images=[[(20000, 4, 32, 32), (126976, 1, 64, 64)]],
@@ -318,6 +328,41 @@ def time_loop(torch, fns, graph, steps: int, warmup: int) -> float:
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
+def measured_ceilings(torch) -> dict:
+    """What the box reaches on plain library work, beside the published peaks the
+    roofline uses: a 1 GiB device-to-device copy (read + write bytes per second)
+    and an 8192^3 bf16 matrix product (torch.mm, contiguous operands)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def best_ms(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            best = min(best, ev[0].elapsed_time(ev[1]))
+        return best
+
+    n = 1 << 30
+    a = torch.empty(n // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    copy_ms = best_ms(lambda: b.copy_(a))
+    del a, b
+    m = 8192
+    x = torch.randn(m, m, device="cuda:0").to(torch.bfloat16)
+    y = torch.randn(m, m, device="cuda:0").to(torch.bfloat16)
+    z = torch.empty(m, m, dtype=torch.bfloat16, device="cuda:0")
+    mm_ms = best_ms(lambda: torch.mm(x, y, out=z))
+    del x, y, z
+    return {"stream_copy_gbps": round(2 * n / (copy_ms * 1e-3) / 1e9, 1),
+            "gemm_bf16_tflops": round(2 * m ** 3 / (mm_ms * 1e-3) / 1e12, 1),
+            "how": "best of 10: a 1 GiB device copy (bytes read + written), torch.mm of two "
+                   "8192x8192 bf16 matrices"}
+
+
 def time_stages(torch, sets, stages, K: int) -> dict:
     """Mean duration (us) of each stage from HIP events recorded on the launch
     stream; the launches queue behind a spin kernel so the GPU runs them back to
@@ -353,6 +398,8 @@ def main() -> int:
     ap.add_argument("--stage-steps", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the copy and matrix-product ceilings measured beside the result")
     ap.add_argument("--no-graph", action="store_true", help="time plain stream launches")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one elementwise kernel over this size (counter calibration)")
@@ -480,6 +527,8 @@ def main() -> int:
     config = {"workload": args.workload, "batch": wl.batch, "seed": wl.seed, "context": cfg["context"],
               "q_heads": 16, "kv_heads": 2, "head_dim": 256, "indexer": "4x128", "topk_blocks": 512,
               "page_size": wl.page_size, "input_sets": len(sets), "launch": launch}
+    if kv == "fp8":
+        config["kv_cache"] = "fp8 e4m3, one scale per pool"
     if cfg.get("images"):
         config["rope"] = "mrope, contiguous sections 16/24/24 of the 64 indexer pairs"
         config["vision_spans"] = [list(map(list, spans)) for spans in cfg["images"]]
@@ -539,8 +588,6 @@ def main() -> int:
                               "traffic": load_traffic(args.workload, dom)}
     else:
         nbytes = decode_bytes(wl, counts, kv_bytes=1 if kv == "fp8" else 2)
-        if kv == "fp8":
-            config["kv_cache"] = "fp8 e4m3, one scale per pool"
         result["value"] = round(wl.batch / (ms_step * 1e-3), 1)
         result["ms_per_step"] = round(ms_step, 5)
         result["step_hbm_gbps"] = round(nbytes["step"] / (ms_step * 1e-3) / 1e9, 1)
@@ -554,6 +601,8 @@ def main() -> int:
                               "frac": round(achieved / HBM_PEAK_GBPS, 4),
                               "traffic": load_traffic(args.workload, dom)}
 
+    if not args.no_ceilings:
+        result["measured_ceilings"] = measured_ceilings(torch)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, kv)
     print(json.dumps(result), flush=True)

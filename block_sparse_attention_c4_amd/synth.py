@@ -337,6 +337,12 @@ def indexshare_b4_l262140(seed: int = 1005) -> Workload:
                          page_order="shuffled", reuse_steps=3)
 
 
+def decode_b8_l131072(seed: int = 1007) -> Workload:
+    """Batch 8 at exactly L = 131072 (32768 complete blocks, no pending token): the
+    literal 128K decode point, shuffled pages."""
+    return make_workload("decode_b8_l131072", "decode", seed, [131072] * 8, page_order="shuffled")
+
+
 def verify_b32_loguniform(seed: int = 1006) -> Workload:
     """Target verification of drafted tokens: batch 32, 4 query tokens per request (the
     capture token plus 3 drafts) at the end of a cache of log-uniform length in
@@ -352,4 +358,5 @@ FULL_SIZE = {
     "prefill_chunk4096_prefix126976": prefill_4096_on_126976,
     "indexshare_b4_l262140": indexshare_b4_l262140,
     "verify_b32x4_loguniform_4k_128k": verify_b32_loguniform,
+    "decode_b8_l131072": decode_b8_l131072,
 }
