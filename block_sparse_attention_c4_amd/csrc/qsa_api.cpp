@@ -100,6 +100,7 @@ static int build_common(const qsa_dims* dims, int32_t batch, const uint16_t* new
   if (batch == 0 || total_new == 0) return QSA_OK;
   if (!new_idx_k || !cu_new || !len_before || !page_table || !ring || !comp_cache) return QSA_E_NULL;
   if (!aligned(new_idx_k, 8) || !aligned(ring, 8) || !aligned(comp_cache, 8)) return QSA_E_SHAPE;
+  if (!aligned(new_mpos, 4) || !aligned(ring_mpos, 4)) return QSA_E_SHAPE;   // NULL passes
   qsa::BuildArgs a;
   a.batch = batch;
   a.max_new = max_new;

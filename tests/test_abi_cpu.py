@@ -122,6 +122,45 @@ def test_gqa_validation():
                                     2052, FAKE, None, None, 0, None) == B.QSA_E_NULL   # q_req missing
 
 
+def test_gqa_fp8_validation():
+    d = B.default_dims()
+    L = B.lib()
+    ws = B.qsa_workspace_bytes(d, B.QSA_OP_GQA_DECODE, 8, 0, 0)
+
+    def dec(**k):
+        return L.qsa_sparse_gqa_decode_fp8(ctypes.byref(d), k.get("batch", 8), FAKE, k.get("k", FAKE),
+                                           k.get("v", FAKE), k.get("ks", 0.01), k.get("vs", 0.02), FAKE, 64,
+                                           FAKE, FAKE, 2052, None, 0, FAKE, None, FAKE, ws, None)
+    assert dec(batch=0) == B.QSA_OK
+    assert dec(k=None) == B.QSA_E_NULL
+    assert dec(v=None) == B.QSA_E_NULL
+    assert dec(k=FAKE + 8) == B.QSA_E_SHAPE                     # 16-byte aligned code rows
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert dec(ks=bad) == B.QSA_E_SHAPE
+        assert dec(vs=bad) == B.QSA_E_SHAPE
+    assert L.qsa_sparse_gqa_prefill_fp8(ctypes.byref(d), 4, FAKE, None, FAKE, FAKE, 1.0, 1.0, FAKE, 64,
+                                        FAKE, FAKE, 2052, FAKE, None, None, 0, None) == B.QSA_E_NULL
+
+
+def test_build_mrope_validation():
+    d = B.default_dims()
+    L = B.lib()
+    contiguous = (ctypes.c_uint8 * 64)(*([0] * 16 + [1] * 24 + [2] * 24))
+
+    def build(axis=contiguous, **k):
+        return L.qsa_build_index_keys_mrope(ctypes.byref(d), k.get("batch", 2), FAKE, k.get("mpos", FAKE),
+                                            FAKE, FAKE, k.get("total", 8), min(4, k.get("total", 8)), FAKE, 64,
+                                            None if axis is None else ctypes.addressof(axis), FAKE,
+                                            k.get("ring_mpos", FAKE), FAKE, None)
+    assert build(total=0) == B.QSA_OK
+    assert build(axis=None) == B.QSA_E_NULL
+    assert build(mpos=None) == B.QSA_E_NULL
+    assert build(ring_mpos=None) == B.QSA_E_NULL
+    assert build(mpos=FAKE + 2) == B.QSA_E_SHAPE                # int32 positions
+    bad = (ctypes.c_uint8 * 64)(*([0] * 63 + [3]))
+    assert build(axis=bad) == B.QSA_E_SHAPE                      # only t, h, w
+
+
 def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(B, "_lib", None)
     monkeypatch.setattr(B, "LIB_PATH", "/nonexistent/libqsa.so")
