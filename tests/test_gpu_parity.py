@@ -167,9 +167,11 @@ MROPE = {
     "mrope_prefill": lambda: synth.with_mrope(
         synth.make_workload("mrope_prefill", "prefill", 317, [3000, 9000], chunk=37),
         [[(100, 1, 16, 16), (2970, 1, 2, 8)], [(5000, 2, 8, 8)]]),
+    # request 4: the decode token 779 completes block 776..779, whose first token (a
+    # vision token of the span 700..776) arrived earlier and waits in the position ring
     "mrope_decode": lambda: synth.with_mrope(
-        synth.make_workload("mrope_decode", "decode", 318, [4099, 777, 2100, 6]),
-        [[(50, 1, 32, 32)], [(700, 1, 7, 11)], [], [(1, 1, 1, 3)]]),
+        synth.make_workload("mrope_decode", "decode", 318, [4099, 777, 2100, 6, 780]),
+        [[(50, 1, 32, 32)], [(700, 1, 7, 11)], [], [(1, 1, 1, 3)], [(700, 1, 7, 11)]]),
     "mrope_interleaved": lambda: synth.with_mrope(
         synth.make_workload("mrope_interleaved", "prefill", 319, [2501, 700], chunk=9),
         [[(1000, 3, 10, 12)], [(690, 1, 3, 3)]], pair_axis=np.arange(64) % 3),
