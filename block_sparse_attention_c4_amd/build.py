@@ -1,6 +1,10 @@
 """Build libqsa.so (the C ABI plus the HIP kernels) for gfx950, in tree.
 
-    python -m block_sparse_attention_c4_amd.build
+    python -m block_sparse_attention_c4_amd.build [--debug]
+
+--debug builds libqsa_debug.so instead: the same library compiled with -DQSA_DEBUG,
+whose kernels trap when device-side contents (page-table entries, positions,
+counts) break their documented ranges.  Point QSA_LIB at it to use it.
 """
 
 from __future__ import annotations
@@ -14,6 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libqsa.so")
+OUT_DEBUG = os.path.join(PKG, "libqsa_debug.so")
 OBJ = os.path.join(ROOT, "_build")
 SOURCES = ["qsa_api.cpp", "qsa_build.hip", "qsa_index.hip", "qsa_topk.hip", "qsa_prefill.hip",
            "qsa_attn.hip"]
@@ -27,30 +32,32 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, debug: bool = False) -> str:
+    obj = os.path.join(OBJ, "debug" if debug else "", os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *(["-DQSA_DEBUG"] if debug else []), "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, debug: bool = False) -> str:
+    out = OUT_DEBUG if debug else OUT
+    os.makedirs(os.path.join(OBJ, "debug" if debug else ""), exist_ok=True)
     with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, debug), SOURCES))
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print("built", OUT)
-    return OUT
+        print("built", out)
+    return out
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, debug="--debug" in sys.argv[1:])
     sys.exit(0)

@@ -280,6 +280,7 @@ attn_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ q_req,
   const int span = min(((sp + 1) * nchunk / splits) * kChunk, bound) - start;
   const int req = q_req ? q_req[t] : t;
   const int cnt = sel_count[t];
+  QSA_CHECK(cnt >= 0 && cnt <= sel_stride);
   const int total = cnt + n_extra;
   const int len = max(0, min(span, total - start));
   // Translate the positions to pool slots (-1 = no position).  All list loads
@@ -302,7 +303,11 @@ attn_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ q_req,
     }
     int pg[kSlotsPer];
 #pragma unroll
-    for (int u = 0; u < kSlotsPer; ++u) pg[u] = p[u] >= 0 ? pt_row[p[u] / page_size] : 0;
+    for (int u = 0; u < kSlotsPer; ++u) {
+      QSA_CHECK(p[u] < pt_stride * page_size);
+      pg[u] = p[u] >= 0 ? pt_row[p[u] / page_size] : 0;
+      QSA_CHECK(pg[u] >= 0);
+    }
 #pragma unroll
     for (int u = 0; u < kSlotsPer; ++u) {
       const int i = tid + u * kThreads;

@@ -53,7 +53,11 @@ build_kernel(const uint16_t* __restrict__ new_k, const int32_t* __restrict__ cu_
   const bool complete = (kBlock * c + kBlock - 1) < le;
   const int bpp = page_size / kBlock;   // compressed rows per page
   int64_t row = 0;
-  if (complete) row = (int64_t)page_table[(size_t)b * pt_stride + c / bpp] * bpp + (c % bpp);
+  QSA_CHECK(lb >= 0 && (le - 1) / page_size < pt_stride);
+  if (complete) {
+    QSA_CHECK(page_table[(size_t)b * pt_stride + c / bpp] >= 0);
+    row = (int64_t)page_table[(size_t)b * pt_stride + c / bpp] * bpp + (c % bpp);
+  }
 
   // read phase: FP32 sum in token order, then * 1/4
   float m[8];

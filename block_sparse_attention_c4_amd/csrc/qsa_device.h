@@ -19,6 +19,20 @@ constexpr int kMaxContext = 262144;
 constexpr int kMaxBlocks = kMaxContext / kBlock;   // 65536
 constexpr int kScoreGroup = 16;  // blocks per group maximum written by the scorer
 
+// Device-side contents (page tables, positions, counts) are trusted.  A build with
+// -DQSA_DEBUG checks the documented ranges where the kernels read them and traps on
+// a violation; the release build compiles the checks away.
+#ifdef QSA_DEBUG
+#define QSA_CHECK(cond) \
+  do {                  \
+    if (!(cond)) __builtin_trap(); \
+  } while (0)
+#else
+#define QSA_CHECK(cond) \
+  do {                  \
+  } while (0)
+#endif
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -150,11 +164,6 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_
 
 __device__ __forceinline__ u32x4_t ld16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
-}
-
-// Slot of logical token t of a request (row of its page table).
-__device__ __forceinline__ int64_t token_slot(const int32_t* pt_row, int t, int page_size) {
-  return (int64_t)pt_row[t / page_size] * page_size + (t % page_size);
 }
 
 }  // namespace qsa

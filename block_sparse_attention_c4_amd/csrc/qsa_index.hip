@@ -71,6 +71,7 @@ score_kernel(int nq, const uint16_t* __restrict__ idx_q, const float* __restrict
   __shared__ int s_tg[kWaveGroups];    // query << 16 | group, per group of the range
   const int lane = threadIdx.x;
   const int my_nc = lane < nq ? (q_pos[lane] + 1) / kBlock : 0;
+  QSA_CHECK(lane >= nq || (q_pos[lane] >= 0 && my_nc <= score_stride));
   const int my_req = lane < nq ? q_req[lane] : 0;
   const int my_groups = (my_nc + kScoreGroup - 1) / kScoreGroup;
   int incl = my_groups;
@@ -106,7 +107,10 @@ score_kernel(int nq, const uint16_t* __restrict__ idx_q, const float* __restrict
   auto pt_load = [&](int i, int (&pg)[4]) {
     const GroupMeta m = meta(i);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pg[r] = m.pt_row[block_of(m, r) / bpp];
+    for (int r = 0; r < 4; ++r) {
+      pg[r] = m.pt_row[block_of(m, r) / bpp];
+      QSA_CHECK(pg[r] >= 0);
+    }
   };
   auto key_load = [&](int i, const int (&pg)[4], u32x4_t (&kv)[4]) {
     const GroupMeta m = meta(i);
@@ -256,6 +260,7 @@ score_multi_kernel(int nq, const uint16_t* __restrict__ idx_q, const float* __re
       const int t = kWin * lane + j;
       wreq[j] = t < nq ? q_req[t] : -1;
       wnc[j] = t < nq ? (q_pos[t] + 1) / kBlock : 0;
+      QSA_CHECK(t >= nq || (q_pos[t] >= 0 && wnc[j] <= score_stride));
       s_req[lane][j] = wreq[j];
       s_nc[lane][j] = wnc[j];
     }
@@ -317,7 +322,11 @@ score_multi_kernel(int nq, const uint16_t* __restrict__ idx_q, const float* __re
     return u;
   };
   auto block_of = [&](const Unit& u) { return min(u.g * kScoreGroup + (lane & 15), u.nc_max - 1); };
-  auto pt_load = [&](const Unit& u) { return u.pt_row[block_of(u) / bpp]; };
+  auto pt_load = [&](const Unit& u) {
+    const int pg = u.pt_row[block_of(u) / bpp];
+    QSA_CHECK(pg >= 0);
+    return pg;
+  };
   auto key_load = [&](const Unit& u, int pg, u32x4_t (&kf)[4]) {
     const int c = block_of(u);
     const uint16_t* krow = comp + ((int64_t)pg * bpp + (c % bpp)) * kIdxDim + 8 * (lane >> 4);

@@ -46,6 +46,7 @@ __device__ __forceinline__ uint32_t score_code(float s) {
 }
 
 __device__ __forceinline__ int64_t comp_row(const int32_t* pt_row, int c, int bpp) {
+  QSA_CHECK(pt_row[c / bpp] >= 0);
   return (int64_t)pt_row[c / bpp] * bpp + (c % bpp);
 }
 
@@ -121,6 +122,7 @@ score_mfma_kernel(int total_q, const uint16_t* __restrict__ idx_q, const float* 
   const bool qv = tq < total_q;
   const int req = qv ? q_req[tq] : -1;
   const int nc = qv ? (q_pos[tq] + 1) / kBlock : 0;
+  QSA_CHECK(!qv || (q_pos[tq] >= 0 && nc <= stride));
   uint64_t remaining = __ballot(qv && nc > c_begin);
   const int fq = tid >> 2, fg = tid & 3;          // flush (tid < 256): query t0 + fq, groups fg + 4k
 
@@ -137,6 +139,7 @@ score_mfma_kernel(int total_q, const uint16_t* __restrict__ idx_q, const float* 
     const int32_t* pt_row = page_table + (size_t)r * pt_stride;
     for (int i = tid; i < n_here; i += kST) {
       const int c = c_begin + i;
+      QSA_CHECK(pt_row[c / bpp] >= 0);
       rows[i] = (uint32_t)pt_row[c / bpp] * (uint32_t)bpp + (uint32_t)(c % bpp);
     }
 
@@ -435,6 +438,7 @@ topk_codes_kernel(const uint16_t* __restrict__ codes, const uint16_t* __restrict
   const int tid = threadIdx.x;
   const int p = q_pos[t];
   const int n = (p + 1) / kBlock;
+  QSA_CHECK(p >= 0 && n <= stride);
   const int pend = (p + 1) % kBlock;
   int32_t* row_b = sel_blocks + (size_t)t * kTopK;
   int32_t* row_p = sel_pos + (size_t)t * sel_stride;

@@ -402,6 +402,7 @@ __device__ __forceinline__ void topk_row(int t, const float* __restrict__ scores
   const int tid = threadIdx.x;
   const int p = q_pos[t];
   const int n = (p + 1) / kBlock;
+  QSA_CHECK(p >= 0 && n <= score_stride);
   const int pend = (p + 1) % kBlock;
   int32_t* row_b = sel_blocks + (size_t)t * kTopK;
   int32_t* row_p = sel_pos + (size_t)t * sel_stride;

@@ -24,7 +24,9 @@
  *  - Host-side arguments are validated before anything is launched; on error a
  *    status other than QSA_OK is returned and nothing is enqueued.  Contents of
  *    device arrays (page tables, positions, counts) are trusted: they must lie
- *    in the ranges stated below.
+ *    in the ranges stated below.  The library built with -DQSA_DEBUG
+ *    (libqsa_debug.so) checks them where the kernels read them and traps the
+ *    kernel on a violation.
  *  - Reentrant; no mutable global state.
  *
  * Supported shapes: num_q_heads = 16, num_kv_heads = 2, head_dim = 256,
