@@ -385,7 +385,8 @@ def time_stages(torch, sets, stages, K: int) -> dict:
         for j, (name, _) in enumerate(stages):
             st[name].append(e[j].elapsed_time(e[j + 1]))
         st["step"].append(e[0].elapsed_time(e[-1]))
-    return {k: float(np.mean(v)) * 1e3 for k, v in st.items()}
+    return {k: float(np.mean(v)) * 1e3 for k, v in st.items()}, \
+        {k: [round(float(np.percentile(v, q)) * 1e3, 2) for q in (10, 50, 90)] for k, v in st.items()}
 
 
 def main() -> int:
@@ -481,8 +482,12 @@ def main() -> int:
     # ---------------- whole steps
     ms_step, launch = timed([step_fn(d) for d in sets], [d.out for d in sets], [ref_out] * len(sets))
     assert torch.equal(sets[(steps - 1) % len(sets)].out, ref_out)
+    # the same steps as plain stream launches, and a warm variant: one input copy
+    # every step, so the last-level cache may serve what the previous step read
+    ms_stream = time_loop(torch, [step_fn(d) for d in sets], None, steps, warmup)
+    ms_warm, _ = timed([step_fn(sets[0])], [sets[0].out], [ref_out])
     stages = [("build", build_fn), ("index", lambda d: d.index()), ("attend", lambda d: d.attend())]
-    stage_us = time_stages(torch, sets, stages, K)
+    stage_us, stage_pct = time_stages(torch, sets, stages, K)
 
     # ---------------- IndexShare: reuse steps j = 1..3 cycled over the input copies
     reuse = None
@@ -509,7 +514,7 @@ def main() -> int:
             torch.cuda.synchronize()
             refs.append(d.out.clone())
         ms_reuse = timed(fns, [d.out for d in sets], refs)[0] / J
-        rst = time_stages(torch, sets, [("reuse", lambda d: d.attend(
+        rst, _ = time_stages(torch, sets, [("reuse", lambda d: d.attend(
             q=d.reuse_q[J - 1], extra=extras[J - 1], n_extra=4))], K)
         reuse = {"ms": ms_reuse, "attend_us": rst["reuse"]}
 
@@ -536,6 +541,13 @@ def main() -> int:
               "warmup": warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
               "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": config}
     result["stage_us"] = {k: round(v, 2) for k, v in stage_us.items()}
+    result["stage_us_p10_p50_p90"] = stage_pct
+    result["ms_per_step_stream_launches"] = round(ms_stream, 5)
+    result["ms_per_step_warm"] = round(ms_warm, 5)
+    result["timing"] = (f"value and ms_per_step: {steps} steps after {warmup} warm-up steps, host clock "
+                        f"around synchronize(), {len(sets)} input copies cycled ({launch}); "
+                        "stage_us: means of HIP events on the launch stream over back-to-back steps; "
+                        "ms_per_step_warm: one input copy, hipGraph replays")
 
     if kind == "prefill":
         work = prefill_work(wl, counts)
