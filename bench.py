@@ -207,6 +207,20 @@ def _oracle_keys_at(O, wl, b: int, prefix_keys, p: int):
     return np.concatenate([prefix_keys, blk])
 
 
+def host_cpu() -> dict:
+    """The host the oracle ran on: CPU model and the processors the OS reports."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count()}
+
+
 def cpu_baseline(wl, seconds: float, kv: str = "bf16") -> dict:
     """The oracle on the same workload, single-threaded, for about `seconds`: decode
     queries over the batch, prefill query rows of the chunk, or IndexShare reuse
@@ -617,6 +631,7 @@ def main() -> int:
         result["measured_ceilings"] = measured_ceilings(torch)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, kv)
+        result["cpu_baseline"]["host"] = host_cpu()
     print(json.dumps(result), flush=True)
     return 0
 
