@@ -413,6 +413,9 @@ def main() -> int:
     ap.add_argument("--stage-steps", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the plain-launch and warm step timings (profiled runs: every traced "
+                         "step is then a cold one)")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the copy and matrix-product ceilings measured beside the result")
     ap.add_argument("--no-graph", action="store_true", help="time plain stream launches")
@@ -498,8 +501,10 @@ def main() -> int:
     assert torch.equal(sets[(steps - 1) % len(sets)].out, ref_out)
     # the same steps as plain stream launches, and a warm variant: one input copy
     # every step, so the last-level cache may serve what the previous step read
-    ms_stream = time_loop(torch, [step_fn(d) for d in sets], None, steps, warmup)
-    ms_warm, _ = timed([step_fn(sets[0])], [sets[0].out], [ref_out])
+    ms_stream = ms_warm = None
+    if not args.headline_only:
+        ms_stream = time_loop(torch, [step_fn(d) for d in sets], None, steps, warmup)
+        ms_warm, _ = timed([step_fn(sets[0])], [sets[0].out], [ref_out])
     stages = [("build", build_fn), ("index", lambda d: d.index()), ("attend", lambda d: d.attend())]
     stage_us, stage_pct = time_stages(torch, sets, stages, K)
 
@@ -556,8 +561,9 @@ def main() -> int:
               "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": config}
     result["stage_us"] = {k: round(v, 2) for k, v in stage_us.items()}
     result["stage_us_p10_p50_p90"] = stage_pct
-    result["ms_per_step_stream_launches"] = round(ms_stream, 5)
-    result["ms_per_step_warm"] = round(ms_warm, 5)
+    if ms_stream is not None:
+        result["ms_per_step_stream_launches"] = round(ms_stream, 5)
+        result["ms_per_step_warm"] = round(ms_warm, 5)
     result["timing"] = (f"value and ms_per_step: {steps} steps after {warmup} warm-up steps, host clock "
                         f"around synchronize(), {len(sets)} input copies cycled ({launch}); "
                         "stage_us: means of HIP events on the launch stream over back-to-back steps; "
