@@ -15,11 +15,12 @@
 // inverse frequencies theta^(-2i/128) come from the host's libm; the angle is
 // reduced to [-pi, pi] with a two-constant Cody-Waite step before sincos.
 //
-// MRoPE [same section: the block is turned with the first token's MRoPE position;
-// the indexer reuses the attention layers' MRoPE]: with 3-D token positions
-// (temporal, height, width), pair i turns by pos[axis(i)] * theta^(-2i/128), the
-// per-pair axis map coming from the host.  The positions of the unfinished
-// block's tokens wait in a position ring beside the key ring.
+// MRoPE [same section: a block's key is rotated by the multimodal rotary position of
+// its first token, and the indexer shares the attention layers' MRoPE code]: with 3-D
+// token positions (temporal, height, width), pair i turns by
+// pos[axis(i)] * theta^(-2i/128), the per-pair axis map coming from the host.  The
+// positions of the unfinished block's tokens wait in a position ring beside the key
+// ring.
 #include "qsa_device.h"
 #include "qsa_launch.h"
 

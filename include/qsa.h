@@ -126,8 +126,8 @@ int qsa_build_index_keys(const qsa_dims* dims, int32_t batch, const uint16_t* ne
 
 /* Stage 1 with MRoPE positions - as qsa_build_index_keys, for models whose tokens
  * carry 3-D rotary positions (temporal, height, width; image and video tokens).
- * [QSA section: the block's mean is turned with the first token's MRoPE position,
- * and the indexer reuses the attention layers' MRoPE implementation.  The pages
+ * [QSA section: a block's key is rotated by the multimodal rotary position of its
+ * first token, and the indexer shares the attention layers' MRoPE code.  The pages
  * give no section layout; the axis map is an argument.]
  *
  * Every step is that of qsa_build_index_keys except the angle: pair (i, i+64) of

@@ -37,8 +37,8 @@ Readings where the pages are silent or garbled (each is listed in the design doc):
       mantissa bits, no infinities, S.1111.111 is NaN, largest finite 448) with one
       scale per pool; a stored code c stands for e4m3(c) * k_scale (K) or
       e4m3(c) * v_scale (V).  Attention is then as in R7 on those values.
-  R10 MRoPE [QSA: the block is turned with "the first token's MRoPE position", and
-      the indexer reuses the attention layers' MRoPE]: a token has a 3-D position
+  R10 MRoPE [QSA: each block's key is rotated by the multimodal rotary position of
+      the block's first token, and the indexer shares the attention layers' MRoPE]: a token has a 3-D position
       (temporal, height, width); each rotary pair i takes the angle
       pos[axis(i)] * theta**(-2i/128) from one component, chosen by a per-pair axis
       map.  The pages give no sections; the default map is contiguous sections of
