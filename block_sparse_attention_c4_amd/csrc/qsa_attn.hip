@@ -1,8 +1,9 @@
 // Stage 3: sparse GQA over the selected positions, read from the raw paged K/V.
 //
 // [SGLang day-0 post on Qwen3.8-Flash-Next, section "Qwen Sparse Attention:
-// Retrieve Coarsely, Attend Precisely"]: the softmax and the value aggregation
-// use the original, uncompressed K/V at the selected logical positions.
+// Retrieve Coarsely, Attend Precisely"]: attention weights and the weighted sum
+// of values are computed from the full-resolution K/V rows of the selected logical
+// positions, not from the compressed keys.
 // [Same post, section "IndexShare MTP: Reusing the QSA Selection Across Draft
 // Steps"]: a draft step attends to the captured selection plus the positions
 // drafted since, passed here as extra positions.

@@ -95,9 +95,9 @@ const char* qsa_status_string(int status);
 size_t qsa_workspace_bytes(const qsa_dims* dims, int op, int32_t total_q, int32_t max_pos,
                            int32_t n_extra);
 
-/* Stage 1 - compressed index-key builder.  [QSA section: every 4 raw index keys
- * are averaged in FP32, normalised, turned with the first token's rotary
- * position and kept as one BF16 compressed key; a 4-slot per-request ring holds
+/* Stage 1 - compressed index-key builder.  [QSA section: each group of 4 raw
+ * indexer keys becomes one BF16 compressed key: their FP32 mean, normalised and
+ * rotated by the block's first-token rotary position; a 4-slot per-request ring holds
  * the raw keys of the unfinished block; compressed keys sit at full_slot / 4.]
  *
  * Ingests the raw indexer keys of new tokens len_before[b] .. len_before[b] +
@@ -152,9 +152,9 @@ int qsa_build_index_keys_mrope(const qsa_dims* dims, int32_t batch, const uint16
                                const uint8_t* pair_axis, uint16_t* ring, int32_t* ring_mpos,
                                uint16_t* comp_cache, void* stream);
 
-/* Stage 2 - indexer: score, top-512, expansion.  [QSA section: a query scores
- * the visible compressed blocks, the best 512 are kept and expanded to 2048
- * token positions, and the 0..3 tokens of the unfinished block are appended,
+/* Stage 2 - indexer: score, top-512, expansion.  [QSA section: every complete
+ * block a query can see gets a score; the 512 highest-scoring blocks become their
+ * 2048 token positions, and the 0..3 tokens of the still-open block are added, for
  * at most 2051 positions.]
  *
  * For query t at position p = q_pos[t] of request b = q_req[t]:
@@ -183,8 +183,8 @@ int qsa_index_topk(const qsa_dims* dims, int32_t batch, int32_t total_q, const u
                    int32_t sel_stride, int32_t* sel_count, void* workspace, size_t ws_bytes,
                    void* stream);
 
-/* Stage 3 - sparse GQA, decode (one query per request).  [QSA section: the
- * final softmax and value aggregation use the original, uncompressed K/V; IndexShare
+/* Stage 3 - sparse GQA, decode (one query per request).  [QSA section: attention
+ * weights and the weighted value sum come from the full-resolution K/V; IndexShare
  * section: a draft step reuses the captured selection plus the positions drafted
  * since the capture.]
  *
