@@ -91,13 +91,14 @@ _CSRC = "block_sparse_attention_c4_amd/csrc/"
 KERNEL_SOURCES = {
     "attend": [_CSRC + f for f in ("qsa_attn.hip", "qsa_device.h", "qsa_launch.h")],
     "index": [_CSRC + f for f in ("qsa_index.hip", "qsa_topk.hip", "qsa_prefill.hip", "qsa_device.h",
-                                  "qsa_launch.h")],
-    "build": [_CSRC + f for f in ("qsa_build.hip", "qsa_device.h", "qsa_launch.h")],
+                                  "qsa_keymath.h", "qsa_launch.h")],
+    "build": [_CSRC + f for f in ("qsa_build.hip", "qsa_device.h", "qsa_keymath.h", "qsa_launch.h")],
 }
-ENTRY = {"build": "qsa_build_index_keys", "index": "qsa_index_topk", "attend": "qsa_sparse_gqa_decode"}
+ENTRY = {"build": "qsa_build_index_keys", "index": "qsa_index_topk", "attend": "qsa_sparse_gqa_decode",
+         "build_index": "qsa_decode_build_index_topk"}
 
 
-def stage_kernels(kind: str, kv: str = "bf16") -> dict:
+def stage_kernels(kind: str, kv: str = "bf16", fused: bool = False) -> dict:
     if kind == "verify":
         return {"build": "build_kernel", "index": "score_multi_kernel + topk_kernel",
                 "attend": "attn_kernel + combine_kernel"}
@@ -105,8 +106,10 @@ def stage_kernels(kind: str, kv: str = "bf16") -> dict:
         return {"build": "build_kernel",
                 "index": "score_mfma_kernel + topk_codes_kernel (+ rescore_kernel, topk_queued_kernel)",
                 "attend": "attn_kernel + combine_kernel"}
-    return {"build": "build_kernel", "index": "score_kernel + topk_kernel",
-            "attend": "attn_kernel<fp8> + combine_kernel" if kv == "fp8" else "attn_kernel + combine_kernel"}
+    attend = "attn_kernel<fp8> + combine_kernel" if kv == "fp8" else "attn_kernel + combine_kernel"
+    if fused:
+        return {"build_index": "score_build_kernel + topk_kernel", "attend": attend}
+    return {"build": "build_kernel", "index": "score_kernel + topk_kernel", "attend": attend}
 
 
 def traffic_file(workload: str) -> str:
@@ -419,6 +422,9 @@ def main() -> int:
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the copy and matrix-product ceilings measured beside the result")
     ap.add_argument("--no-graph", action="store_true", help="time plain stream launches")
+    ap.add_argument("--unfused", action="store_true",
+                    help="decode: run the builder and the indexer as two calls (by default one "
+                         "qsa_decode_build_index_topk call does both)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one elementwise kernel over this size (counter calibration)")
     args = ap.parse_args()
@@ -463,9 +469,12 @@ def main() -> int:
         for d in sets:
             d.ring_saved = d.ring.clone()
 
-    def step_fn(d):
+    # decode steps ingest each request's token inside the indexer call
+    fused = kind in ("decode", "indexshare") and not args.unfused and base.can_fuse()
+
+    def step_fn(d, fused=fused):
         if not restore:
-            return d.step
+            return lambda: d.step(fused=fused)
 
         def run():
             d.ring.copy_(d.ring_saved)
@@ -505,7 +514,13 @@ def main() -> int:
     if not args.headline_only:
         ms_stream = time_loop(torch, [step_fn(d) for d in sets], None, steps, warmup)
         ms_warm, _ = timed([step_fn(sets[0])], [sets[0].out], [ref_out])
-    stages = [("build", build_fn), ("index", lambda d: d.index()), ("attend", lambda d: d.attend())]
+    ms_unfused = None
+    if fused and not args.headline_only:
+        ms_unfused, _ = timed([step_fn(d, False) for d in sets], [d.out for d in sets], [ref_out] * len(sets))
+    if fused:
+        stages = [("build_index", lambda d: d.build_index()), ("attend", lambda d: d.attend())]
+    else:
+        stages = [("build", build_fn), ("index", lambda d: d.index()), ("attend", lambda d: d.attend())]
     stage_us, stage_pct = time_stages(torch, sets, stages, K)
 
     # ---------------- IndexShare: reuse steps j = 1..3 cycled over the input copies
@@ -547,12 +562,15 @@ def main() -> int:
         torch.mul(a, 1.0, out=b)
         torch.cuda.synchronize()
 
-    kernels = stage_kernels(kind, kv)
+    kernels = stage_kernels(kind, kv, fused)
     config = {"workload": args.workload, "batch": wl.batch, "seed": wl.seed, "context": cfg["context"],
               "q_heads": 16, "kv_heads": 2, "head_dim": 256, "indexer": "4x128", "topk_blocks": 512,
               "page_size": wl.page_size, "input_sets": len(sets), "launch": launch}
     if kv == "fp8":
         config["kv_cache"] = "fp8 e4m3, one scale per pool"
+    if kind in ("decode", "indexshare"):
+        config["builder"] = ("folded into the indexer call (qsa_decode_build_index_topk)" if fused
+                             else "its own call (qsa_build_index_keys)")
     if cfg.get("images"):
         config["rope"] = "mrope, contiguous sections 16/24/24 of the 64 indexer pairs"
         config["vision_spans"] = [list(map(list, spans)) for spans in cfg["images"]]
@@ -564,10 +582,13 @@ def main() -> int:
     if ms_stream is not None:
         result["ms_per_step_stream_launches"] = round(ms_stream, 5)
         result["ms_per_step_warm"] = round(ms_warm, 5)
+    if ms_unfused is not None:
+        result["ms_per_step_builder_separate"] = round(ms_unfused, 5)
     result["timing"] = (f"value and ms_per_step: {steps} steps after {warmup} warm-up steps, host clock "
                         f"around synchronize(), {len(sets)} input copies cycled ({launch}); "
                         "stage_us: means of HIP events on the launch stream over back-to-back steps; "
-                        "ms_per_step_warm: one input copy, hipGraph replays")
+                        "ms_per_step_warm: one input copy, hipGraph replays; "
+                        "ms_per_step_builder_separate: the same steps with the builder as its own call")
 
     if kind == "prefill":
         work = prefill_work(wl, counts)

@@ -34,7 +34,7 @@ QSA_MAX_EXTRA = 8
 
 EXPORTED = ["qsa_status_string", "qsa_workspace_bytes", "qsa_build_index_keys", "qsa_index_topk",
             "qsa_sparse_gqa_decode", "qsa_sparse_gqa_prefill", "qsa_sparse_gqa_decode_fp8",
-            "qsa_sparse_gqa_prefill_fp8", "qsa_build_index_keys_mrope"]
+            "qsa_sparse_gqa_prefill_fp8", "qsa_build_index_keys_mrope", "qsa_decode_build_index_topk"]
 
 
 class QsaError(RuntimeError):
@@ -94,6 +94,9 @@ def lib() -> ctypes.CDLL:
         L.qsa_build_index_keys_mrope.restype = ctypes.c_int
         L.qsa_build_index_keys_mrope.argtypes = [ctypes.POINTER(QsaDims), _I, _P, _P, _P, _P, _I, _I,
                                                  _P, _I, _P, _P, _P, _P, _P]
+        L.qsa_decode_build_index_topk.restype = ctypes.c_int
+        L.qsa_decode_build_index_topk.argtypes = [ctypes.POINTER(QsaDims), _I, _P, _P, _I, _P, _I, _P,
+                                                  _P, _P, _P, _P, _P, _I, _P, _P, _SZ, _P]
         _lib = L
     return _lib
 
@@ -147,6 +150,17 @@ def qsa_index_topk(dims, batch, total_q, idx_q, idx_w, q_req, q_pos, max_pos, pa
                               _ptr(comp_cache), _ptr(sel_blocks), _ptr(sel_pos), sel_stride,
                               _ptr(sel_count), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "qsa_index_topk")
+
+
+def qsa_decode_build_index_topk(dims, batch, new_idx_k, pos, max_pos, page_table, pt_stride, ring,
+                                comp_cache, idx_q, idx_w, sel_blocks, sel_pos, sel_stride, sel_count,
+                                workspace, ws_bytes, stream=None) -> None:
+    st = lib().qsa_decode_build_index_topk(ctypes.byref(dims), batch, _ptr(new_idx_k), _ptr(pos), max_pos,
+                                           _ptr(page_table), pt_stride, _ptr(ring), _ptr(comp_cache),
+                                           _ptr(idx_q), _ptr(idx_w), _ptr(sel_blocks), _ptr(sel_pos),
+                                           sel_stride, _ptr(sel_count), _ptr(workspace), ws_bytes,
+                                           _stream(stream))
+    _check(st, "qsa_decode_build_index_topk")
 
 
 def qsa_sparse_gqa_decode(dims, batch, q, k_pool, v_pool, page_table, pt_stride, sel_pos, sel_count,

@@ -159,6 +159,50 @@ int qsa_index_topk(const qsa_dims* dims, int32_t batch, int32_t total_q, const u
   return hip_status(qsa::launch_index(a, static_cast<hipStream_t>(stream)));
 }
 
+int qsa_decode_build_index_topk(const qsa_dims* dims, int32_t batch, const uint16_t* new_idx_k,
+                                const int32_t* pos, int32_t max_pos, const int32_t* page_table,
+                                int32_t pt_stride, uint16_t* ring, uint16_t* comp_cache,
+                                const uint16_t* idx_q, const float* idx_w, int32_t* sel_blocks,
+                                int32_t* sel_pos, int32_t sel_stride, int32_t* sel_count,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st != QSA_OK) return st;
+  if (batch < 1 || batch > 65535 || max_pos < 1 || max_pos > QSA_MAX_CONTEXT || pt_stride < 1 ||
+      sel_stride < QSA_MAX_SEL)
+    return QSA_E_SHAPE;
+  if (!new_idx_k || !pos || !page_table || !ring || !comp_cache || !idx_q || !idx_w ||
+      !sel_blocks || !sel_pos || !sel_count)
+    return QSA_E_NULL;
+  if (!aligned(new_idx_k, 8) || !aligned(ring, 8) || !aligned(idx_q, 16) ||
+      !aligned(comp_cache, 16) || !aligned(sel_pos, 16) || sel_stride % 4 != 0)
+    return QSA_E_SHAPE;
+  const size_t need = qsa::index_workspace_bytes(batch, max_pos);
+  if (!workspace || ws_bytes < need || !aligned(workspace, 256)) return QSA_E_WORKSPACE;
+  qsa::IndexArgs a;
+  a.batch = batch;
+  a.total_q = batch;
+  a.max_pos = max_pos;
+  a.page_size = dims->page_size;
+  a.pt_stride = pt_stride;
+  a.sel_stride = sel_stride;
+  a.idx_q = idx_q;
+  a.idx_w = idx_w;
+  a.q_req = nullptr;
+  a.q_pos = pos;
+  a.page_table = page_table;
+  a.comp = comp_cache;
+  a.sel_blocks = sel_blocks;
+  a.sel_pos = sel_pos;
+  a.sel_count = sel_count;
+  qsa::index_workspace_carve(a, workspace);
+  qsa::IngestArgs f;
+  f.new_k = new_idx_k;
+  f.ring = ring;
+  f.comp = comp_cache;
+  f.theta = dims->rope_theta;
+  return hip_status(qsa::launch_index_ingest(a, f, static_cast<hipStream_t>(stream)));
+}
+
 // fp8: the pools hold E4M3 codes scaled by k_scale / v_scale (finite and > 0).
 static int gqa_common(const qsa_dims* dims, int32_t total_q, const uint16_t* q,
                       const int32_t* q_req, const void* k_pool, const void* v_pool, bool fp8,

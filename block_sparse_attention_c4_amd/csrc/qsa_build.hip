@@ -6,14 +6,9 @@
 // token; the result is one bf16 key stored at the block's first slot / 4.  The raw
 // keys of the unfinished block wait in a 4-slot ring per request.
 //
-// One wave per work group handles 4 blocks, 16 lanes per block.  Lane j (0..15)
-// of a block owns rotary pairs i = 4j .. 4j+3, i.e. dims 4j..4j+3 and
-// 64+4j..64+4j+3, so every rotation is lane local.  The mean is taken in FP32 in
-// token order (as the pages fix); the norm, the rotation and the rounding are
-// done in FP64, which keeps the phase exact to well below a bf16 step even at
-// position 262140 (an FP32 angle would be off by up to ~0.016 rad there).  The
-// inverse frequencies theta^(-2i/128) come from the host's libm; the angle is
-// reduced to [-pi, pi] with a two-constant Cody-Waite step before sincos.
+// One wave per work group handles 4 blocks, 16 lanes per block; the key arithmetic
+// (FP32 mean in token order, FP64 norm and rotation, bf16 rounding) is in
+// qsa_keymath.h.  The inverse frequencies theta^(-2i/128) come from the host's libm.
 //
 // MRoPE [same section: a block's key is rotated by the multimodal rotary position of
 // its first token, and the indexer shares the attention layers' MRoPE code]: with 3-D
@@ -22,6 +17,7 @@
 // positions of the unfinished block's tokens wait in a position ring beside the key
 // ring.
 #include "qsa_device.h"
+#include "qsa_keymath.h"
 #include "qsa_launch.h"
 
 #include <cmath>
@@ -31,9 +27,6 @@ namespace qsa {
 namespace {
 
 constexpr int kUnits = 4;   // blocks per work group
-constexpr double kTwoPiHi = 6.283185307179586;          // 2*pi rounded to double
-constexpr double kTwoPiLo = 2.4492935982947064e-16;     // 2*pi - kTwoPiHi
-constexpr double kInvTwoPi = 0.15915494309189535;
 
 __global__ void __launch_bounds__(64)
 build_kernel(const uint16_t* __restrict__ new_k, const int32_t* __restrict__ cu_new,
@@ -60,23 +53,17 @@ build_kernel(const uint16_t* __restrict__ new_k, const int32_t* __restrict__ cu_
     row = (int64_t)page_table[(size_t)b * pt_stride + c / bpp] * bpp + (c % bpp);
   }
 
-  // read phase: FP32 sum in token order, then * 1/4
+  // read phase: FP32 mean in token order
   float m[8];
   if (complete) {
+    const uint16_t* src[kBlock];
 #pragma unroll
     for (int tok = 0; tok < kBlock; ++tok) {
       const int t = kBlock * c + tok;
-      const uint16_t* src = (t < lb) ? ring + ((size_t)b * kBlock + (t & 3)) * kIdxDim
-                                     : new_k + (size_t)(off + t - lb) * kIdxDim;
-      const u32x2_t a = *reinterpret_cast<const u32x2_t*>(src + 4 * j);
-      const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(src + 64 + 4 * j);
-      const float v[8] = {bf16lo(a.x), bf16hi(a.x), bf16lo(a.y), bf16hi(a.y),
-                          bf16lo(bb.x), bf16hi(bb.x), bf16lo(bb.y), bf16hi(bb.y)};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) m[e] = (tok == 0) ? v[e] : (m[e] + v[e]);
+      src[tok] = (t < lb) ? ring + ((size_t)b * kBlock + (t & 3)) * kIdxDim
+                          : new_k + (size_t)(off + t - lb) * kIdxDim;
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) m[e] = m[e] * 0.25f;
+    key_block_mean(src, j, m);
   }
   // 3-D position of the block's first token (slot 0 of the ring when it is older
   // than this call)
@@ -104,42 +91,13 @@ build_kernel(const uint16_t* __restrict__ new_k, const int32_t* __restrict__ cu_
   }
   if (!complete) return;
 
-  // L2 norm in FP64 over the 16 lanes of this block
-  double md[8];
-  double ss = 0.0;
+  double ppos[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    md[e] = (double)m[e];
-    ss += md[e] * md[e];
-  }
-#pragma unroll
-  for (int sh = 1; sh < 16; sh <<= 1) ss += __shfl_xor(ss, sh, 64);
-  const double nrm = fmax(sqrt(ss), 1e-12);
-
-  const double pos = (double)(kBlock * c);
-  uint32_t outw[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int i = 4 * j + e;
-    const double x = (new_mpos ? (double)p3[rope.axis[i]] : pos) * rope.inv_freq[i];
-    const double k = rint(x * kInvTwoPi);
-    double red = fma(-k, kTwoPiHi, x);
-    red = fma(-k, kTwoPiLo, red);
-    double s, co;
-    sincos(red, &s, &co);
-    const double a = md[e] / nrm;
-    const double bv = md[4 + e] / nrm;
-    const double y0 = a * co - bv * s;
-    const double y1 = bv * co + a * s;
-    outw[e] = f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
-  }
-  // outw[e] packs (dim 4j+e, dim 64+4j+e); store dims 4j..4j+3 and 64+4j..+3
-  uint16_t* dst = comp + row * kIdxDim;
+  for (int e = 0; e < 4; ++e)
+    ppos[e] = new_mpos ? (double)p3[rope.axis[4 * j + e]] : (double)(kBlock * c);
   u32x2_t lo, hi;
-  lo.x = (outw[0] & 0xffffu) | (outw[1] << 16);
-  lo.y = (outw[2] & 0xffffu) | (outw[3] << 16);
-  hi.x = (outw[0] >> 16) | (outw[1] & 0xffff0000u);
-  hi.y = (outw[2] >> 16) | (outw[3] & 0xffff0000u);
+  key_rotate(m, ppos, rope.inv_freq, j, lo, hi);
+  uint16_t* dst = comp + row * kIdxDim;
   *reinterpret_cast<u32x2_t*>(dst + 4 * j) = lo;
   *reinterpret_cast<u32x2_t*>(dst + 64 + 4 * j) = hi;
 }

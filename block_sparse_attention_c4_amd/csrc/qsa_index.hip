@@ -18,7 +18,10 @@
 // tokens per request]: the queries of a request share each key load.  Top-512
 // selection and expansion live in qsa_topk.hip.
 #include "qsa_device.h"
+#include "qsa_keymath.h"
 #include "qsa_launch.h"
+
+#include <cmath>
 
 namespace qsa {
 
@@ -49,6 +52,14 @@ __device__ __forceinline__ int groups_of(int p) {
 // ping-pong register set; scores stay in LDS until the range is done.  With no
 // store in flight the in-order load counter lets each wait cover exactly the loads
 // it needs, so three groups' loads overlap.
+//
+// A decode step can also ingest each request's new token in the same launch
+// (score_build_kernel).  The first nq work groups then belong one to each query:
+// query t's group writes the token to its ring slot or, when the token completes a
+// block, builds that block's key with the builder's arithmetic (qsa_keymath.h),
+// stores it, and scores the query's last 16-block group, which holds the new block,
+// with the key taken from LDS.  The other work groups score every group but the
+// last of each query.  No work group reads memory that another one writes.
 constexpr int kWaveGroups = 64;
 
 struct GroupMeta {
@@ -61,19 +72,32 @@ struct QueryRows {
   float w[kIdxHeads];
 };
 
-__global__ void __launch_bounds__(64)
-score_kernel(int nq, const uint16_t* __restrict__ idx_q, const float* __restrict__ idx_w,
-             const int32_t* __restrict__ q_req, const int32_t* __restrict__ q_pos,
-             const int32_t* __restrict__ page_table, int pt_stride, int page_size,
-             const uint16_t* __restrict__ comp, float* __restrict__ scores, int score_stride,
-             float* __restrict__ gmax) {
+// The step's new tokens (score_build_kernel): query t of the launch is request
+// req0 + t, and its own token, at position q_pos[t], is the one ingested.
+struct Ingest {
+  const uint16_t* new_k;   // [nq, 128] raw indexer keys of those tokens
+  uint16_t* ring;          // [batch, 4, 128] pending-token ring
+  uint16_t* comp;          // the compressed key cache (the new blocks' rows are written)
+  int req0;
+  RopeTable rope;
+};
+
+template <bool kIngest>
+__device__ __forceinline__ void score_body(
+    int nq, const uint16_t* __restrict__ idx_q, const float* __restrict__ idx_w,
+    const int32_t* __restrict__ q_req, const int32_t* __restrict__ q_pos,
+    const int32_t* __restrict__ page_table, int pt_stride, int page_size,
+    const uint16_t* __restrict__ comp, float* __restrict__ scores, int score_stride,
+    float* __restrict__ gmax, const Ingest* ing) {
   __shared__ float s_out[kWaveGroups * kScoreGroup];
   __shared__ int s_tg[kWaveGroups];    // query << 16 | group, per group of the range
   const int lane = threadIdx.x;
   const int my_nc = lane < nq ? (q_pos[lane] + 1) / kBlock : 0;
   QSA_CHECK(lane >= nq || (q_pos[lane] >= 0 && my_nc <= score_stride));
-  const int my_req = lane < nq ? q_req[lane] : 0;
-  const int my_groups = (my_nc + kScoreGroup - 1) / kScoreGroup;
+  const int my_req = lane < nq ? (kIngest ? ing->req0 + lane : q_req[lane]) : 0;
+  const int all_groups = (my_nc + kScoreGroup - 1) / kScoreGroup;
+  // with kIngest the last group of a query is left to the query's own work group
+  const int my_groups = kIngest ? max(all_groups - 1, 0) : all_groups;
   int incl = my_groups;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -82,15 +106,12 @@ score_kernel(int nq, const uint16_t* __restrict__ idx_q, const float* __restrict
   }
   const int excl = incl - my_groups;
   const int total = __shfl(incl, 63, 64);
-  const int wave = blockIdx.x, nwaves = gridDim.x;
-  const int g_begin = (int)(((int64_t)total * wave) / nwaves);
-  const int g_end = (int)(((int64_t)total * (wave + 1)) / nwaves);
-  const int ng = g_end - g_begin;      // <= kWaveGroups (the launch sizes the grid for it)
-  if (ng <= 0) return;
 
   const int d0 = (lane & 15) * 8;
   const int row_in_step = lane >> 4;
   const int bpp = page_size / kBlock;
+  int g_begin = 0;
+  int ng = 0;
 
   auto meta = [&](int i) {             // group g_begin + i: i wave-uniform, every lane active
     GroupMeta m;
@@ -146,35 +167,108 @@ score_kernel(int nq, const uint16_t* __restrict__ idx_q, const float* __restrict
     }
   };
 
-  // pipeline: at step i the page entries of group i+2 and the keys of group i+1 are
-  // requested, then group i is scored
-  int pg0[4], pg1[4];
-  u32x4_t kv0[4], kv1[4];
-  QueryRows q0, q1;
-  int t0 = meta(0).t;
-  query_load(t0, q0);
-  pt_load(0, pg0);
-  if (ng > 1) pt_load(1, pg1);
-  key_load(0, pg0, kv0);
-  int tq1 = t0;
-  for (int i = 0; i < ng; i += 2) {
-    // even step: group i in kv0 / q0
-    if (i + 2 < ng) pt_load(i + 2, pg0);
-    if (i + 1 < ng) {
-      tq1 = meta(i + 1).t;
-      if (tq1 != t0) query_load(tq1, q1); else q1 = q0;
-      key_load(i + 1, pg1, kv1);
+  if (kIngest && (int)blockIdx.x < nq) {
+    // ---- query t's own work group: its token, then its last group
+    const int t = blockIdx.x;
+    const int b = ing->req0 + t;
+    const int p = q_pos[t];
+    const int n_c = (p + 1) / kBlock;
+    const bool fresh = ((p + 1) % kBlock) == 0;   // the token completes block n_c - 1
+    const uint16_t* nk = ing->new_k + (size_t)t * kIdxDim;
+    uint16_t* rb = ing->ring + (size_t)b * kBlock * kIdxDim;
+    QSA_CHECK(p >= 0 && p / page_size < pt_stride);
+    if (!fresh)   // the token waits in ring slot p % 4 until its block completes
+      reinterpret_cast<uint32_t*>(rb + (p % kBlock) * kIdxDim)[lane] =
+          reinterpret_cast<const uint32_t*>(nk)[lane];   // 64 lanes x 2 bf16
+    if (n_c == 0) return;
+    GroupMeta m;
+    m.t = t;
+    m.g = (n_c - 1) / kScoreGroup;
+    m.n_c = n_c;
+    m.pt_row = page_table + (size_t)b * pt_stride;
+    int pg[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pg[r] = m.pt_row[block_of(m, r) / bpp];
+      QSA_CHECK(pg[r] >= 0);
     }
-    compute(i, kv0, q0);
-    if (i + 1 >= ng) break;
-    // odd step: group i+1 in kv1 / q1
-    if (i + 3 < ng) pt_load(i + 3, pg1);
-    if (i + 2 < ng) {
-      t0 = meta(i + 2).t;
-      if (t0 != tq1) query_load(t0, q0); else q0 = q1;
-      key_load(i + 2, pg0, kv0);
+    QueryRows q;
+    query_load(t, q);
+    const int j = lane & 15;
+    float mean[8];
+    if (fresh) {   // tokens 4c..4c+2 wait in ring slots 0..2, token 4c+3 is the new one
+      const uint16_t* src[kBlock] = {rb, rb + kIdxDim, rb + 2 * kIdxDim, nk};
+      key_block_mean(src, j, mean);
     }
-    compute(i + 1, kv1, q1);
+    u32x4_t kv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {   // the new block's row is stale here; it is replaced below
+      const int c = block_of(m, r);
+      kv[r] = ld16(ing->comp + ((int64_t)pg[r] * bpp + (c % bpp)) * kIdxDim + d0);
+    }
+    if (fresh) {
+      __shared__ __attribute__((aligned(16))) u32x2_t s_key[kIdxDim / 4];
+      const int c = n_c - 1;
+      const double pos = (double)(kBlock * c);
+      const double ppos[4] = {pos, pos, pos, pos};
+      u32x2_t lo, hi;
+      key_rotate(mean, ppos, ing->rope.inv_freq, j, lo, hi);
+      if (lane < 16) {
+        const int64_t row = (int64_t)m.pt_row[c / bpp] * bpp + (c % bpp);
+        uint16_t* dst = ing->comp + row * kIdxDim;
+        *reinterpret_cast<u32x2_t*>(dst + 4 * j) = lo;
+        *reinterpret_cast<u32x2_t*>(dst + 64 + 4 * j) = hi;
+        s_key[j] = lo;          // dims 4j..4j+3
+        s_key[16 + j] = hi;     // dims 64+4j..64+4j+3
+      }
+      __syncthreads();
+      const u32x4_t nkey = *reinterpret_cast<const u32x4_t*>(
+          reinterpret_cast<const uint16_t*>(s_key) + d0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (block_of(m, r) == c) kv[r] = nkey;
+    }
+    if (lane == 0) s_tg[0] = (t << 16) | m.g;
+    compute(0, kv, q);
+    ng = 1;
+  } else {
+    const int wave = blockIdx.x - (kIngest ? nq : 0);
+    const int nwaves = gridDim.x - (kIngest ? nq : 0);
+    g_begin = (int)(((int64_t)total * wave) / nwaves);
+    const int g_end = (int)(((int64_t)total * (wave + 1)) / nwaves);
+    ng = g_end - g_begin;              // <= kWaveGroups (the launch sizes the grid for it)
+    if (ng <= 0) return;
+
+    // pipeline: at step i the page entries of group i+2 and the keys of group i+1
+    // are requested, then group i is scored
+    int pg0[4], pg1[4];
+    u32x4_t kv0[4], kv1[4];
+    QueryRows q0, q1;
+    int t0 = meta(0).t;
+    query_load(t0, q0);
+    pt_load(0, pg0);
+    if (ng > 1) pt_load(1, pg1);
+    key_load(0, pg0, kv0);
+    int tq1 = t0;
+    for (int i = 0; i < ng; i += 2) {
+      // even step: group i in kv0 / q0
+      if (i + 2 < ng) pt_load(i + 2, pg0);
+      if (i + 1 < ng) {
+        tq1 = meta(i + 1).t;
+        if (tq1 != t0) query_load(tq1, q1); else q1 = q0;
+        key_load(i + 1, pg1, kv1);
+      }
+      compute(i, kv0, q0);
+      if (i + 1 >= ng) break;
+      // odd step: group i+1 in kv1 / q1
+      if (i + 3 < ng) pt_load(i + 3, pg1);
+      if (i + 2 < ng) {
+        t0 = meta(i + 2).t;
+        if (t0 != tq1) query_load(t0, q0); else q0 = q1;
+        key_load(i + 2, pg0, kv0);
+      }
+      compute(i + 1, kv1, q1);
+    }
   }
 
   // write the range's scores and each group's maximum: lane l covers group l / 4,
@@ -203,6 +297,26 @@ score_kernel(int nq, const uint16_t* __restrict__ idx_q, const float* __restrict
       }
     }
   }
+}
+
+__global__ void __launch_bounds__(64)
+score_kernel(int nq, const uint16_t* __restrict__ idx_q, const float* __restrict__ idx_w,
+             const int32_t* __restrict__ q_req, const int32_t* __restrict__ q_pos,
+             const int32_t* __restrict__ page_table, int pt_stride, int page_size,
+             const uint16_t* __restrict__ comp, float* __restrict__ scores, int score_stride,
+             float* __restrict__ gmax) {
+  score_body<false>(nq, idx_q, idx_w, q_req, q_pos, page_table, pt_stride, page_size, comp,
+                    scores, score_stride, gmax, nullptr);
+}
+
+__global__ void __launch_bounds__(64)
+score_build_kernel(int nq, const uint16_t* __restrict__ idx_q, const float* __restrict__ idx_w,
+                   const int32_t* __restrict__ q_pos, const int32_t* __restrict__ page_table,
+                   int pt_stride, int page_size, const uint16_t* __restrict__ comp,
+                   float* __restrict__ scores, int score_stride, float* __restrict__ gmax,
+                   Ingest ing) {
+  score_body<true>(nq, idx_q, idx_w, nullptr, q_pos, page_table, pt_stride, page_size, comp,
+                   scores, score_stride, gmax, &ing);
 }
 
 // ------------------------------------------------------------------ multi-query scorer
@@ -471,6 +585,37 @@ hipError_t launch_index(const IndexArgs& a, hipStream_t stream) {
                        a.q_req + q0, a.q_pos + q0, a.page_table, a.pt_stride, a.page_size, a.comp,
                        a.scores + (size_t)q0 * a.score_stride, a.score_stride,
                        a.gmax_f + (size_t)q0 * (a.score_stride / kScoreGroup));
+  }
+  launch_topk(a, stream);
+  return hipGetLastError();
+}
+
+// A decode step with its builder folded in: query t is request t and its own token
+// (position q_pos[t]) is ingested by the scorer launch (score_build_kernel).
+hipError_t launch_index_ingest(const IndexArgs& a, const IngestArgs& f, hipStream_t stream) {
+  Ingest ing;
+  for (int i = 0; i < kIdxDim / 2; ++i) {
+    ing.rope.inv_freq[i] = std::pow((double)f.theta, -(2.0 * i) / (double)kIdxDim);
+    ing.rope.axis[i] = 0;
+  }
+  ing.ring = f.ring;
+  ing.comp = f.comp;
+  const int64_t gpq = (a.max_pos / kBlock + kScoreGroup - 1) / kScoreGroup;
+  constexpr int kQPerLaunch = 64;
+  for (int q0 = 0; q0 < a.total_q; q0 += kQPerLaunch) {
+    const int nq = std::min(kQPerLaunch, a.total_q - q0);
+    const int64_t groups_bound = (int64_t)nq * gpq;
+    const int64_t want = std::min<int64_t>(groups_bound / 2, 4096);
+    const int grid = (int)std::max<int64_t>(
+        1, std::max<int64_t>(want, (groups_bound + kWaveGroups - 1) / kWaveGroups));
+    ing.new_k = f.new_k + (size_t)q0 * kIdxDim;
+    ing.req0 = q0;
+    // nq work groups of the queries' own, then the scorer's
+    hipLaunchKernelGGL(score_build_kernel, dim3(nq + grid), dim3(64), 0, stream, nq,
+                       a.idx_q + (size_t)q0 * kIdxHeads * kIdxDim, a.idx_w + (size_t)q0 * kIdxHeads,
+                       a.q_pos + q0, a.page_table, a.pt_stride, a.page_size, a.comp,
+                       a.scores + (size_t)q0 * a.score_stride, a.score_stride,
+                       a.gmax_f + (size_t)q0 * (a.score_stride / kScoreGroup), ing);
   }
   launch_topk(a, stream);
   return hipGetLastError();

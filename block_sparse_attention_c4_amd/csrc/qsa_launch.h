@@ -49,6 +49,15 @@ struct IndexArgs {
 size_t index_workspace_bytes(int total_q, int max_pos);
 void index_workspace_carve(IndexArgs& a, void* ws);
 hipError_t launch_index(const IndexArgs& a, hipStream_t stream);
+// Decode step whose queries' own tokens are ingested by the scorer launch: query t
+// is request t, its token sits at q_pos[t] (q_req unused).
+struct IngestArgs {
+  const uint16_t* new_k;     // [total_q, 128] raw indexer keys of the queries' tokens
+  uint16_t* ring;            // [total_q, 4, 128]
+  uint16_t* comp;            // the compressed key cache (same memory as IndexArgs::comp)
+  float theta;
+};
+hipError_t launch_index_ingest(const IndexArgs& a, const IngestArgs& f, hipStream_t stream);
 hipError_t launch_index_mfma(const IndexArgs& a, hipStream_t stream);
 void launch_topk(const IndexArgs& a, hipStream_t stream);
 void launch_topk_queued(const IndexArgs& a, hipStream_t stream);

@@ -116,6 +116,22 @@ class DeviceWorkload:
                                self.step_len_before, self.step_total, self.step_max, self.page_table,
                                self.pt_stride, self.ring, self.comp, stream)
 
+    def can_fuse(self) -> bool:
+        """A decode step whose builder can be folded into the indexer call: one new
+        token per request, which is also the request's query (1-D RoPE)."""
+        wl = self.wl
+        return (wl.mpos is None and self.T == self.batch and self.step_total == self.batch
+                and self.step_max == 1 and np.array_equal(wl.q_req, np.arange(self.batch))
+                and np.array_equal(wl.q_pos, wl.prefix_len))
+
+    def build_index(self, stream=None) -> None:
+        """Builder and indexer of a decode step in one call (qsa_decode_build_index_topk)."""
+        B.qsa_decode_build_index_topk(self.dims, self.batch, self.step_new_k, self.step_len_before,
+                                      self.max_pos, self.page_table, self.pt_stride, self.ring,
+                                      self.comp, self.idx_q, self.idx_w, self.sel_blocks,
+                                      self.sel_pos, SEL_STRIDE, self.sel_count, self.ws_index,
+                                      self.ws_index_bytes, stream)
+
     def index(self, stream=None) -> None:
         B.qsa_index_topk(self.dims, self.batch, self.T, self.idx_q, self.idx_w, self.q_req, self.q_pos,
                          self.max_pos, self.page_table, self.pt_stride, self.comp, self.sel_blocks,
@@ -146,10 +162,14 @@ class DeviceWorkload:
                                     SEL_STRIDE, extra, n_extra, self.out, self.lse, self.ws_attn,
                                     self.ws_attn_bytes, stream)
 
-    def step(self, stream=None) -> None:
-        """One pass of the hot path: builder, indexer, sparse GQA."""
-        self.build_step(stream)
-        self.index(stream)
+    def step(self, stream=None, fused: bool = False) -> None:
+        """One pass of the hot path: builder, indexer, sparse GQA.  fused: the builder
+        and the indexer as one call (decode steps that can_fuse())."""
+        if fused:
+            self.build_index(stream)
+        else:
+            self.build_step(stream)
+            self.index(stream)
         self.attend(stream)
 
     def set_reuse(self, j: int) -> None:

@@ -183,6 +183,43 @@ int qsa_index_topk(const qsa_dims* dims, int32_t batch, int32_t total_q, const u
                    int32_t sel_stride, int32_t* sel_count, void* workspace, size_t ws_bytes,
                    void* stream);
 
+/* Stages 1 + 2 of one decode step in two launches instead of three.  [QSA section:
+ * during decode the new token's indexer key enters the ring, or completes a block
+ * whose compressed key is stored, before the query scores the visible blocks; the
+ * pages lay this bookkeeping out as separate kernels ahead of the indexer.]
+ *
+ * Request b has exactly one new token, at position p = pos[b] (the tokens before it:
+ * 0 .. p-1 are already ingested), and that token is also the request's query.  The
+ * call has the effect of
+ *     qsa_build_index_keys(cu_new = 0, 1, .., batch; len_before = pos; total_new =
+ *                          batch; max_new = 1)
+ * followed by
+ *     qsa_index_topk(total_q = batch; q_req[b] = b; q_pos = pos)
+ * and writes the same ring, comp_cache, sel_blocks, sel_pos and sel_count bits as
+ * those two calls.  The scorer launch ingests the tokens itself: each query's own
+ * work group builds the key of a block its token completes and scores the query's
+ * last 16 blocks with it.  1-D RoPE only (no MRoPE positions).
+ *
+ *   new_idx_k  [batch, idx_dim] bf16  raw indexer key of each request's new token
+ *              (8-byte aligned)
+ *   pos        [batch] int32          position of that token (>= 0)
+ *   max_pos (host)                    > every pos; <= QSA_MAX_CONTEXT
+ *   page_table [batch, pt_stride]     must cover position pos[b] of every request
+ *   ring, comp_cache                  in/out, as for qsa_build_index_keys; a block
+ *                                     row written here must not be read by another
+ *                                     request's query of the same call (distinct
+ *                                     requests do not share a page being written)
+ *   idx_q, idx_w                      [batch, ...] as for qsa_index_topk
+ *   sel_blocks, sel_pos, sel_stride, sel_count   out, as for qsa_index_topk
+ *   workspace  >= qsa_workspace_bytes(QSA_OP_INDEX_TOPK, batch, max_pos, 0)
+ */
+int qsa_decode_build_index_topk(const qsa_dims* dims, int32_t batch, const uint16_t* new_idx_k,
+                                const int32_t* pos, int32_t max_pos, const int32_t* page_table,
+                                int32_t pt_stride, uint16_t* ring, uint16_t* comp_cache,
+                                const uint16_t* idx_q, const float* idx_w, int32_t* sel_blocks,
+                                int32_t* sel_pos, int32_t sel_stride, int32_t* sel_count,
+                                void* workspace, size_t ws_bytes, void* stream);
+
 /* Stage 3 - sparse GQA, decode (one query per request).  [QSA section: attention
  * weights and the weighted value sum come from the full-resolution K/V; IndexShare
  * section: a draft step reuses the captured selection plus the positions drafted

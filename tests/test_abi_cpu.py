@@ -83,6 +83,42 @@ def test_index_topk_validation():
                                   None, None, 0, None) == B.QSA_E_NULL
 
 
+def _fused(dims=None, **kw):
+    d = dims or B.default_dims()
+    a = dict(batch=2, new=FAKE, pos=FAKE, max_pos=4096, page_table=FAKE, pt_stride=64, ring=FAKE,
+             comp=FAKE, idx_q=FAKE, idx_w=FAKE, sel_blocks=FAKE, sel_pos=FAKE, sel_stride=2052,
+             sel_count=FAKE, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return B.lib().qsa_decode_build_index_topk(
+        ctypes.byref(d), a["batch"], a["new"], a["pos"], a["max_pos"], a["page_table"], a["pt_stride"],
+        a["ring"], a["comp"], a["idx_q"], a["idx_w"], a["sel_blocks"], a["sel_pos"], a["sel_stride"],
+        a["sel_count"], a["ws"], a["ws_bytes"], None)
+
+
+def test_decode_build_index_topk_validation():
+    assert _fused(batch=0) == B.QSA_E_SHAPE
+    assert _fused(batch=65536) == B.QSA_E_SHAPE
+    assert _fused(max_pos=0) == B.QSA_E_SHAPE
+    assert _fused(max_pos=262145) == B.QSA_E_SHAPE
+    assert _fused(pt_stride=0) == B.QSA_E_SHAPE
+    assert _fused(sel_stride=2050) == B.QSA_E_SHAPE
+    assert _fused(sel_stride=2054) == B.QSA_E_SHAPE
+    for k in ("new", "pos", "page_table", "ring", "comp", "idx_q", "idx_w", "sel_blocks", "sel_pos",
+              "sel_count"):
+        assert _fused(**{k: None}) == B.QSA_E_NULL, k
+    assert _fused(new=FAKE + 4) == B.QSA_E_SHAPE               # raw keys read 8 bytes at a time
+    assert _fused(ring=FAKE + 4) == B.QSA_E_SHAPE
+    assert _fused(comp=FAKE + 8) == B.QSA_E_SHAPE
+    assert _fused(idx_q=FAKE + 8) == B.QSA_E_SHAPE
+    assert _fused(ws=None) == B.QSA_E_WORKSPACE
+    assert _fused(ws_bytes=B.qsa_workspace_bytes(B.default_dims(), B.QSA_OP_INDEX_TOPK, 2, 4096) - 1) \
+        == B.QSA_E_WORKSPACE
+    assert _fused(ws=FAKE + 64) == B.QSA_E_WORKSPACE
+    bad = B.default_dims()
+    bad.idx_heads = 8
+    assert _fused(dims=bad) == B.QSA_E_UNSUPPORTED
+
+
 def test_build_validation():
     d = B.default_dims()
     L = B.lib()

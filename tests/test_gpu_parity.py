@@ -460,3 +460,115 @@ def test_repeat_runs_are_bitwise_identical():
     torch.cuda.synchronize()
     for a, b in zip(first, (dw.comp, dw.sel_blocks, dw.sel_pos, dw.sel_count, dw.out, dw.lse)):
         assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ builder folded into the indexer
+
+# decode lengths for the folded call: tokens that complete a block whose group holds
+# only that block (n_c = 16k + 1), that fill a group (n_c = 16k), the first block
+# (p = 3), no visible block (p < 3), tokens left pending, n_c around 512
+FUSED_SMALL = {
+    "decode_fresh_edges": lambda: synth.make_workload(
+        "decode_fresh_edges", "decode", 316,
+        [1, 3, 4, 5, 8, 64, 68, 1028, 2048, 2052, 4096 + 4, 4096 + 7, 32768, 32772, 40001],
+        hot_per_req=2),
+}
+
+
+def fused_small(name):
+    key = "fused:" + name
+    if key not in _CACHE:
+        _CACHE[key] = FUSED_SMALL[name]()
+    return _CACHE[key]
+
+
+def _decode_names_small():
+    return ["decode_ragged", "decode_page16", "decode_batch70", "indexshare_small"]
+
+
+def _decode_names_full():
+    return [n for n in synth.FULL_SIZE if n.startswith("decode") or n.startswith("indexshare")]
+
+
+def _valid_scores(dw, wl):
+    """The FP32 score rows of the index workspace, cut to each query's visible blocks."""
+    nb = (dw.max_pos + 3) // 4
+    stride = (nb + 127) // 128 * 128
+    sc = dw.ws_index[: wl.total_q * stride * 4].view(torch.float32).view(wl.total_q, stride).cpu().numpy()
+    return [sc[t, : (int(wl.q_pos[t]) + 1) // 4].copy() for t in range(wl.total_q)]
+
+
+def _check_fused_equals_separate(wl):
+    sep = _device(wl)
+    assert sep.can_fuse()
+    sep.build_prefix()
+    sep.build_step()
+    sep.index()
+    torch.cuda.synchronize()
+    fus = _device(wl)
+    fus.build_prefix()
+    fus.build_index()
+    torch.cuda.synchronize()
+    for name in ("comp", "ring", "sel_blocks", "sel_pos", "sel_count"):
+        assert torch.equal(getattr(sep, name), getattr(fus, name)), f"{wl.name}: {name} differs"
+    for t, (a, b) in enumerate(zip(_valid_scores(sep, wl), _valid_scores(fus, wl))):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"{wl.name}: scores of row {t}"
+    P.log(f"[fused] {wl.name}: builder + indexer in one call bit-identical to the two calls")
+
+
+@pytest.mark.parametrize("name", list(FUSED_SMALL))
+def test_fused_build_index_edges(name):
+    _check_fused_equals_separate(fused_small(name))
+
+
+@pytest.mark.parametrize("name", _decode_names_small())
+def test_fused_build_index_small(name):
+    _check_fused_equals_separate(small(name))
+
+
+@pytest.mark.parametrize("name", _decode_names_full())
+def test_fused_build_index_full(name):
+    _check_fused_equals_separate(full(name))
+
+
+def test_fused_max_context():
+    _check_fused_equals_separate(synth.make_workload("maxctx_fused", "decode", 308, [262144, 262143],
+                                                     hot_per_req=16))
+
+
+def _check_e2e_fused(wl):
+    """The folded decode step (one call for builder and indexer, then attention)
+    against the oracle."""
+    dw = _device(wl)
+    dw.build_prefix()
+    dw.step(fused=True)
+    torch.cuda.synchronize()
+    states = P.oracle_index_states(wl)
+    P.check_comp_cache(wl, dw.comp_numpy(), states)
+    P.check_ring(dw.ring_numpy(), states)
+    res = O.run_queries(wl)
+    gb = dw.sel_blocks.cpu().numpy()
+    gp = dw.sel_pos.cpu().numpy()
+    gc = dw.sel_count.cpu().numpy()
+    out = dw.out_f64()
+    lse = dw.lse.cpu().numpy()
+    differing = 0
+    for t in range(wl.total_q):
+        where = f"{wl.name} row {t} (fused)"
+        if P.check_selection(gb[t], res[t], where):
+            P.check_positions(gp[t], int(gc[t]), res[t], where)
+            P.check_attention(out[t], lse[t], res[t], where)
+        else:
+            differing += 1
+            P.check_positions_valid(gp[t], int(gc[t]), gb[t], int(wl.q_pos[t]), where)
+    assert differing <= max(1, wl.total_q // 50), f"{differing} rows with tie-swapped selections"
+    P.log(f"[e2e fused] {wl.name}: {wl.total_q} rows, {differing} tie-swapped")
+
+
+@pytest.mark.parametrize("name", list(FUSED_SMALL))
+def test_end_to_end_fused_edges(name):
+    _check_e2e_fused(fused_small(name))
+
+
+def test_end_to_end_fused_full():
+    _check_e2e_fused(full("decode_b32_loguniform_4k_128k"))
