@@ -93,6 +93,8 @@ KERNEL_SOURCES = {
     "index": [_CSRC + f for f in ("qsa_index.hip", "qsa_topk.hip", "qsa_prefill.hip", "qsa_device.h",
                                   "qsa_keymath.h", "qsa_launch.h")],
     "build": [_CSRC + f for f in ("qsa_build.hip", "qsa_device.h", "qsa_keymath.h", "qsa_launch.h")],
+    "build_index": [_CSRC + f for f in ("qsa_index.hip", "qsa_topk.hip", "qsa_device.h", "qsa_keymath.h",
+                                        "qsa_launch.h")],
 }
 ENTRY = {"build": "qsa_build_index_keys", "index": "qsa_index_topk", "attend": "qsa_sparse_gqa_decode",
          "build_index": "qsa_decode_build_index_topk"}

@@ -605,7 +605,8 @@ hipError_t launch_index_ingest(const IndexArgs& a, const IngestArgs& f, hipStrea
   for (int q0 = 0; q0 < a.total_q; q0 += kQPerLaunch) {
     const int nq = std::min(kQPerLaunch, a.total_q - q0);
     const int64_t groups_bound = (int64_t)nq * gpq;
-    const int64_t want = std::min<int64_t>(groups_bound / 2, 4096);
+    // 4096 waves fill the GPU at 4 per SIMD: the queries' own work groups take nq of them
+    const int64_t want = std::min<int64_t>(groups_bound / 2, 4096 - nq);
     const int grid = (int)std::max<int64_t>(
         1, std::max<int64_t>(want, (groups_bound + kWaveGroups - 1) / kWaveGroups));
     ing.new_k = f.new_k + (size_t)q0 * kIdxDim;
