@@ -62,6 +62,14 @@ def test_graph_decode_step(kv):
     _replays_match(dw, dw.step, _outputs(dw))
 
 
+def test_graph_decode_step_builder_folded():
+    # the decode step as the benchmark runs it: builder and indexer in one call
+    wl = synth.make_workload("g_decode_f", "decode", 333, [4, 5, 2052, 9003, 40000, 700], hot_per_req=2)
+    dw = _device(wl)
+    assert dw.can_fuse()
+    _replays_match(dw, lambda: dw.step(fused=True), _outputs(dw))
+
+
 def test_graph_prefill_step():
     # chunks that start on block boundaries: a repeated step reads the same ring
     wl = synth.make_workload("g_prefill", "prefill", 331, [2104, 9000], chunk=40)
