@@ -382,6 +382,52 @@ def measured_ceilings(torch) -> dict:
                    "8192x8192 bf16 matrices"}
 
 
+def projection_overlap(torch, sets, hidden: int, timed, ref_out) -> dict:
+    """A decode step beside a stand-in for the layer's Q/K/V projection, whose output
+    the indexer does not need: x[batch, hidden] x W[hidden, 5120] in bf16 (16 + 2 + 2
+    heads of 256; synthetic weights, the product is discarded).  Sequential: the
+    projection, then builder + indexer, then attention, on one stream.  Overlapped:
+    builder + indexer on a second stream (default priority) while the projection runs,
+    joined before attention.  Both as hipGraphs of one step per input copy."""
+    dev = sets[0].dev
+    B = sets[0].batch
+    x = torch.randn(B, hidden, device=dev).to(torch.bfloat16)
+    w = (torch.randn(hidden, 5120, device=dev) * hidden ** -0.5).to(torch.bfloat16)
+    y = torch.empty(B, 5120, dtype=torch.bfloat16, device=dev)
+    side = torch.cuda.Stream()
+    torch.mm(x, w, out=y)
+    torch.cuda.synchronize()
+
+    def seq(d):
+        def run():
+            torch.mm(x, w, out=y)
+            d.build_index()
+            d.attend()
+        return run
+
+    def par(d):
+        def run():
+            cur = torch.cuda.current_stream()
+            side.wait_stream(cur)
+            with torch.cuda.stream(side):
+                d.build_index()
+            torch.mm(x, w, out=y)
+            cur.wait_stream(side)
+            d.attend()
+        return run
+
+    outs = [d.out for d in sets]
+    refs = [ref_out] * len(sets)
+    ms_proj, _ = timed([lambda: torch.mm(x, w, out=y)] * len(sets), [], [])
+    ms_seq, _ = timed([seq(d) for d in sets], outs, refs)
+    ms_par, _ = timed([par(d) for d in sets], outs, refs)
+    return {"hidden": hidden, "proj_cols": 5120, "proj_alone_us": round(ms_proj * 1e3, 2),
+            "ms_per_step_sequential": round(ms_seq, 5), "ms_per_step_overlapped": round(ms_par, 5),
+            "how": "stand-in projection torch.mm bf16 on the launch stream; builder + indexer "
+                   "(qsa_decode_build_index_topk) on a second default-priority stream; hipGraph "
+                   "replays, outputs checked against the eager step"}
+
+
 def time_stages(torch, sets, stages, K: int) -> dict:
     """Mean duration (us) of each stage from HIP events recorded on the launch
     stream; the launches queue behind a spin kernel so the GPU runs them back to
@@ -424,6 +470,10 @@ def main() -> int:
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the copy and matrix-product ceilings measured beside the result")
     ap.add_argument("--no-graph", action="store_true", help="time plain stream launches")
+    ap.add_argument("--projection-overlap", type=int, default=0, metavar="HIDDEN",
+                    help="decode: also time the step beside a stand-in Q/K/V projection "
+                         "([batch, HIDDEN] x [HIDDEN, 5120] bf16), once in sequence and once with the "
+                         "builder + indexer on a second stream overlapping it")
     ap.add_argument("--unfused", action="store_true",
                     help="decode: run the builder and the indexer as two calls (by default one "
                          "qsa_decode_build_index_topk call does both)")
@@ -525,6 +575,11 @@ def main() -> int:
         stages = [("build", build_fn), ("index", lambda d: d.index()), ("attend", lambda d: d.attend())]
     stage_us, stage_pct = time_stages(torch, sets, stages, K)
 
+    # ---------------- the indexer on a second stream beside a projection
+    overlap = None
+    if fused and args.projection_overlap > 0:
+        overlap = projection_overlap(torch, sets, args.projection_overlap, timed, ref_out)
+
     # ---------------- IndexShare: reuse steps j = 1..3 cycled over the input copies
     reuse = None
     if kind == "indexshare":
@@ -586,6 +641,8 @@ def main() -> int:
         result["ms_per_step_warm"] = round(ms_warm, 5)
     if ms_unfused is not None:
         result["ms_per_step_builder_separate"] = round(ms_unfused, 5)
+    if overlap is not None:
+        result["projection_overlap"] = overlap
     result["timing"] = (f"value and ms_per_step: {steps} steps after {warmup} warm-up steps, host clock "
                         f"around synchronize(), {len(sets)} input copies cycled ({launch}); "
                         "stage_us: means of HIP events on the launch stream over back-to-back steps; "
