@@ -70,6 +70,28 @@ def test_graph_decode_step_builder_folded():
     _replays_match(dw, lambda: dw.step(fused=True), _outputs(dw))
 
 
+def test_graph_decode_step_indexer_on_second_stream():
+    # builder + indexer on a second stream beside unrelated work on the launch stream,
+    # joined before attention, as one captured graph
+    wl = synth.make_workload("g_decode_s", "decode", 334, [8, 2051, 9003, 40000, 703], hot_per_req=2)
+    dw = _device(wl)
+    x = torch.randn(64, 1024, device=dw.dev).to(torch.bfloat16)
+    w = torch.randn(1024, 1024, device=dw.dev).to(torch.bfloat16)
+    y = torch.empty(64, 1024, dtype=torch.bfloat16, device=dw.dev)
+    side = torch.cuda.Stream()
+
+    def step():
+        cur = torch.cuda.current_stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            dw.build_index()
+        torch.mm(x, w, out=y)
+        cur.wait_stream(side)
+        dw.attend()
+
+    _replays_match(dw, step, _outputs(dw))
+
+
 def test_graph_prefill_step():
     # chunks that start on block boundaries: a repeated step reads the same ring
     wl = synth.make_workload("g_prefill", "prefill", 331, [2104, 9000], chunk=40)
