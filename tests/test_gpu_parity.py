@@ -472,6 +472,10 @@ FUSED_SMALL = {
         "decode_fresh_edges", "decode", 316,
         [1, 3, 4, 5, 8, 64, 68, 1028, 2048, 2052, 4096 + 4, 4096 + 7, 32768, 32772, 40001],
         hot_per_req=2),
+    # no request with a complete block: the launch's scorer part has no group at all
+    "decode_no_blocks": lambda: synth.make_workload("decode_no_blocks", "decode", 317, [1, 2, 3]),
+    # one block at most: the only groups are the queries' own
+    "decode_one_block": lambda: synth.make_workload("decode_one_block", "decode", 318, [4, 1, 5, 2]),
 }
 
 
