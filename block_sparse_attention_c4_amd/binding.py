@@ -34,7 +34,8 @@ QSA_MAX_EXTRA = 8
 
 EXPORTED = ["qsa_status_string", "qsa_workspace_bytes", "qsa_build_index_keys", "qsa_index_topk",
             "qsa_sparse_gqa_decode", "qsa_sparse_gqa_prefill", "qsa_sparse_gqa_decode_fp8",
-            "qsa_sparse_gqa_prefill_fp8", "qsa_build_index_keys_mrope", "qsa_decode_build_index_topk"]
+            "qsa_sparse_gqa_prefill_fp8", "qsa_build_index_keys_mrope", "qsa_decode_build_index_topk",
+            "qsa_decode_build_index_topk_mrope"]
 
 
 class QsaError(RuntimeError):
@@ -97,6 +98,10 @@ def lib() -> ctypes.CDLL:
         L.qsa_decode_build_index_topk.restype = ctypes.c_int
         L.qsa_decode_build_index_topk.argtypes = [ctypes.POINTER(QsaDims), _I, _P, _P, _I, _P, _I, _P,
                                                   _P, _P, _P, _P, _P, _I, _P, _P, _SZ, _P]
+        L.qsa_decode_build_index_topk_mrope.restype = ctypes.c_int
+        L.qsa_decode_build_index_topk_mrope.argtypes = [ctypes.POINTER(QsaDims), _I, _P, _P, _P, _I, _P,
+                                                        _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P,
+                                                        _P, _SZ, _P]
         _lib = L
     return _lib
 
@@ -161,6 +166,20 @@ def qsa_decode_build_index_topk(dims, batch, new_idx_k, pos, max_pos, page_table
                                            sel_stride, _ptr(sel_count), _ptr(workspace), ws_bytes,
                                            _stream(stream))
     _check(st, "qsa_decode_build_index_topk")
+
+
+def qsa_decode_build_index_topk_mrope(dims, batch, new_idx_k, new_mpos, pos, max_pos, page_table,
+                                      pt_stride, pair_axis, ring, ring_mpos, comp_cache, idx_q, idx_w,
+                                      sel_blocks, sel_pos, sel_stride, sel_count, workspace, ws_bytes,
+                                      stream=None) -> None:
+    """pair_axis: 64 host values (0 temporal, 1 height, 2 width), e.g. a numpy array."""
+    axis = (ctypes.c_uint8 * 64)(*[int(v) for v in pair_axis])
+    st = lib().qsa_decode_build_index_topk_mrope(
+        ctypes.byref(dims), batch, _ptr(new_idx_k), _ptr(new_mpos), _ptr(pos), max_pos, _ptr(page_table),
+        pt_stride, ctypes.addressof(axis), _ptr(ring), _ptr(ring_mpos), _ptr(comp_cache), _ptr(idx_q),
+        _ptr(idx_w), _ptr(sel_blocks), _ptr(sel_pos), sel_stride, _ptr(sel_count), _ptr(workspace),
+        ws_bytes, _stream(stream))
+    _check(st, "qsa_decode_build_index_topk_mrope")
 
 
 def qsa_sparse_gqa_decode(dims, batch, q, k_pool, v_pool, page_table, pt_stride, sel_pos, sel_count,

@@ -159,12 +159,14 @@ int qsa_index_topk(const qsa_dims* dims, int32_t batch, int32_t total_q, const u
   return hip_status(qsa::launch_index(a, static_cast<hipStream_t>(stream)));
 }
 
-int qsa_decode_build_index_topk(const qsa_dims* dims, int32_t batch, const uint16_t* new_idx_k,
-                                const int32_t* pos, int32_t max_pos, const int32_t* page_table,
-                                int32_t pt_stride, uint16_t* ring, uint16_t* comp_cache,
-                                const uint16_t* idx_q, const float* idx_w, int32_t* sel_blocks,
-                                int32_t* sel_pos, int32_t sel_stride, int32_t* sel_count,
-                                void* workspace, size_t ws_bytes, void* stream) {
+static int decode_build_index_common(const qsa_dims* dims, int32_t batch,
+                                     const uint16_t* new_idx_k, const int32_t* new_mpos,
+                                     const int32_t* pos, int32_t max_pos, const int32_t* page_table,
+                                     int32_t pt_stride, const uint8_t* pair_axis, uint16_t* ring,
+                                     int32_t* ring_mpos, uint16_t* comp_cache, const uint16_t* idx_q,
+                                     const float* idx_w, int32_t* sel_blocks, int32_t* sel_pos,
+                                     int32_t sel_stride, int32_t* sel_count, void* workspace,
+                                     size_t ws_bytes, void* stream) {
   int st = check_dims(dims);
   if (st != QSA_OK) return st;
   if (batch < 1 || batch > 65535 || max_pos < 1 || max_pos > QSA_MAX_CONTEXT || pt_stride < 1 ||
@@ -174,7 +176,8 @@ int qsa_decode_build_index_topk(const qsa_dims* dims, int32_t batch, const uint1
       !sel_blocks || !sel_pos || !sel_count)
     return QSA_E_NULL;
   if (!aligned(new_idx_k, 8) || !aligned(ring, 8) || !aligned(idx_q, 16) ||
-      !aligned(comp_cache, 16) || !aligned(sel_pos, 16) || sel_stride % 4 != 0)
+      !aligned(comp_cache, 16) || !aligned(sel_pos, 16) || sel_stride % 4 != 0 ||
+      !aligned(new_mpos, 4) || !aligned(ring_mpos, 4))   // NULL passes
     return QSA_E_SHAPE;
   const size_t need = qsa::index_workspace_bytes(batch, max_pos);
   if (!workspace || ws_bytes < need || !aligned(workspace, 256)) return QSA_E_WORKSPACE;
@@ -200,7 +203,40 @@ int qsa_decode_build_index_topk(const qsa_dims* dims, int32_t batch, const uint1
   f.ring = ring;
   f.comp = comp_cache;
   f.theta = dims->rope_theta;
+  f.new_mpos = new_mpos;
+  f.ring_mpos = ring_mpos;
+  f.pair_axis = pair_axis;
   return hip_status(qsa::launch_index_ingest(a, f, static_cast<hipStream_t>(stream)));
+}
+
+int qsa_decode_build_index_topk(const qsa_dims* dims, int32_t batch, const uint16_t* new_idx_k,
+                                const int32_t* pos, int32_t max_pos, const int32_t* page_table,
+                                int32_t pt_stride, uint16_t* ring, uint16_t* comp_cache,
+                                const uint16_t* idx_q, const float* idx_w, int32_t* sel_blocks,
+                                int32_t* sel_pos, int32_t sel_stride, int32_t* sel_count,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  return decode_build_index_common(dims, batch, new_idx_k, nullptr, pos, max_pos, page_table,
+                                   pt_stride, nullptr, ring, nullptr, comp_cache, idx_q, idx_w,
+                                   sel_blocks, sel_pos, sel_stride, sel_count, workspace, ws_bytes,
+                                   stream);
+}
+
+int qsa_decode_build_index_topk_mrope(const qsa_dims* dims, int32_t batch,
+                                      const uint16_t* new_idx_k, const int32_t* new_mpos,
+                                      const int32_t* pos, int32_t max_pos,
+                                      const int32_t* page_table, int32_t pt_stride,
+                                      const uint8_t* pair_axis, uint16_t* ring, int32_t* ring_mpos,
+                                      uint16_t* comp_cache, const uint16_t* idx_q,
+                                      const float* idx_w, int32_t* sel_blocks, int32_t* sel_pos,
+                                      int32_t sel_stride, int32_t* sel_count, void* workspace,
+                                      size_t ws_bytes, void* stream) {
+  if (!pair_axis || !new_mpos || !ring_mpos) return QSA_E_NULL;
+  for (int i = 0; i < 64; ++i)
+    if (pair_axis[i] > 2) return QSA_E_SHAPE;
+  return decode_build_index_common(dims, batch, new_idx_k, new_mpos, pos, max_pos, page_table,
+                                   pt_stride, pair_axis, ring, ring_mpos, comp_cache, idx_q, idx_w,
+                                   sel_blocks, sel_pos, sel_stride, sel_count, workspace, ws_bytes,
+                                   stream);
 }
 
 // fp8: the pools hold E4M3 codes scaled by k_scale / v_scale (finite and > 0).

@@ -78,6 +78,8 @@ struct Ingest {
   const uint16_t* new_k;   // [nq, 128] raw indexer keys of those tokens
   uint16_t* ring;          // [batch, 4, 128] pending-token ring
   uint16_t* comp;          // the compressed key cache (the new blocks' rows are written)
+  const int32_t* new_mpos; // [nq, 3] MRoPE positions of those tokens, or NULL (1-D RoPE)
+  int32_t* ring_mpos;      // [batch, 4, 3] positions of the ring's tokens (MRoPE only)
   int req0;
   RopeTable rope;
 };
@@ -177,9 +179,13 @@ __device__ __forceinline__ void score_body(
     const uint16_t* nk = ing->new_k + (size_t)t * kIdxDim;
     uint16_t* rb = ing->ring + (size_t)b * kBlock * kIdxDim;
     QSA_CHECK(p >= 0 && p / page_size < pt_stride);
-    if (!fresh)   // the token waits in ring slot p % 4 until its block completes
+    if (!fresh) {   // the token waits in ring slot p % 4 until its block completes
       reinterpret_cast<uint32_t*>(rb + (p % kBlock) * kIdxDim)[lane] =
           reinterpret_cast<const uint32_t*>(nk)[lane];   // 64 lanes x 2 bf16
+      if (ing->new_mpos && lane < 3)
+        ing->ring_mpos[((size_t)b * kBlock + (p % kBlock)) * 3 + lane] =
+            ing->new_mpos[(size_t)t * 3 + lane];
+    }
     if (n_c == 0) return;
     GroupMeta m;
     m.t = t;
@@ -209,8 +215,15 @@ __device__ __forceinline__ void score_body(
     if (fresh) {
       __shared__ __attribute__((aligned(16))) u32x2_t s_key[kIdxDim / 4];
       const int c = n_c - 1;
-      const double pos = (double)(kBlock * c);
-      const double ppos[4] = {pos, pos, pos, pos};
+      double ppos[4];
+      if (ing->new_mpos) {   // 3-D position of token 4c, which waits in ring slot 0
+        const int32_t* p3 = ing->ring_mpos + (size_t)b * kBlock * 3;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ppos[e] = (double)p3[ing->rope.axis[4 * j + e]];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ppos[e] = (double)(kBlock * c);
+      }
       u32x2_t lo, hi;
       key_rotate(mean, ppos, ing->rope.inv_freq, j, lo, hi);
       if (lane < 16) {
@@ -596,10 +609,11 @@ hipError_t launch_index_ingest(const IndexArgs& a, const IngestArgs& f, hipStrea
   Ingest ing;
   for (int i = 0; i < kIdxDim / 2; ++i) {
     ing.rope.inv_freq[i] = std::pow((double)f.theta, -(2.0 * i) / (double)kIdxDim);
-    ing.rope.axis[i] = 0;
+    ing.rope.axis[i] = f.pair_axis ? f.pair_axis[i] : 0;
   }
   ing.ring = f.ring;
   ing.comp = f.comp;
+  ing.ring_mpos = f.ring_mpos;
   const int64_t gpq = (a.max_pos / kBlock + kScoreGroup - 1) / kScoreGroup;
   constexpr int kQPerLaunch = 64;
   for (int q0 = 0; q0 < a.total_q; q0 += kQPerLaunch) {
@@ -610,6 +624,7 @@ hipError_t launch_index_ingest(const IndexArgs& a, const IngestArgs& f, hipStrea
     const int grid = (int)std::max<int64_t>(
         1, std::max<int64_t>(want, (groups_bound + kWaveGroups - 1) / kWaveGroups));
     ing.new_k = f.new_k + (size_t)q0 * kIdxDim;
+    ing.new_mpos = f.new_mpos ? f.new_mpos + (size_t)q0 * 3 : nullptr;
     ing.req0 = q0;
     // nq work groups of the queries' own, then the scorer's
     hipLaunchKernelGGL(score_build_kernel, dim3(nq + grid), dim3(64), 0, stream, nq,

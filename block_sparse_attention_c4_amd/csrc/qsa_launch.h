@@ -56,6 +56,9 @@ struct IngestArgs {
   uint16_t* ring;            // [total_q, 4, 128]
   uint16_t* comp;            // the compressed key cache (same memory as IndexArgs::comp)
   float theta;
+  const int32_t* new_mpos;   // [total_q, 3] MRoPE positions of the tokens, or NULL (1-D RoPE)
+  int32_t* ring_mpos;        // [total_q, 4, 3] (MRoPE only)
+  const uint8_t* pair_axis;  // host [64] (MRoPE only)
 };
 hipError_t launch_index_ingest(const IndexArgs& a, const IngestArgs& f, hipStream_t stream);
 hipError_t launch_index_mfma(const IndexArgs& a, hipStream_t stream);

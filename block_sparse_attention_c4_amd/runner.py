@@ -118,14 +118,22 @@ class DeviceWorkload:
 
     def can_fuse(self) -> bool:
         """A decode step whose builder can be folded into the indexer call: one new
-        token per request, which is also the request's query (1-D RoPE)."""
+        token per request, which is also the request's query."""
         wl = self.wl
-        return (wl.mpos is None and self.T == self.batch and self.step_total == self.batch
+        return (self.T == self.batch and self.step_total == self.batch
                 and self.step_max == 1 and np.array_equal(wl.q_req, np.arange(self.batch))
                 and np.array_equal(wl.q_pos, wl.prefix_len))
 
     def build_index(self, stream=None) -> None:
-        """Builder and indexer of a decode step in one call (qsa_decode_build_index_topk)."""
+        """Builder and indexer of a decode step in one call (qsa_decode_build_index_topk,
+        or its MRoPE form)."""
+        if self.wl.mpos is not None:
+            B.qsa_decode_build_index_topk_mrope(
+                self.dims, self.batch, self.step_new_k, self.step_mpos, self.step_len_before,
+                self.max_pos, self.page_table, self.pt_stride, self.wl.pair_axis, self.ring,
+                self.ring_mpos, self.comp, self.idx_q, self.idx_w, self.sel_blocks, self.sel_pos,
+                SEL_STRIDE, self.sel_count, self.ws_index, self.ws_index_bytes, stream)
+            return
         B.qsa_decode_build_index_topk(self.dims, self.batch, self.step_new_k, self.step_len_before,
                                       self.max_pos, self.page_table, self.pt_stride, self.ring,
                                       self.comp, self.idx_q, self.idx_w, self.sel_blocks,

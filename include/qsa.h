@@ -198,7 +198,8 @@ int qsa_index_topk(const qsa_dims* dims, int32_t batch, int32_t total_q, const u
  * and writes the same ring, comp_cache, sel_blocks, sel_pos and sel_count bits as
  * those two calls.  The scorer launch ingests the tokens itself: each query's own
  * work group builds the key of a block its token completes and scores the query's
- * last 16 blocks with it.  1-D RoPE only (no MRoPE positions).
+ * last 16 blocks with it.  1-D RoPE (qsa_decode_build_index_topk_mrope takes 3-D
+ * positions).
  *
  *   new_idx_k  [batch, idx_dim] bf16  raw indexer key of each request's new token
  *              (8-byte aligned)
@@ -219,6 +220,31 @@ int qsa_decode_build_index_topk(const qsa_dims* dims, int32_t batch, const uint1
                                 const uint16_t* idx_q, const float* idx_w, int32_t* sel_blocks,
                                 int32_t* sel_pos, int32_t sel_stride, int32_t* sel_count,
                                 void* workspace, size_t ws_bytes, void* stream);
+
+/* Stages 1 + 2 of one decode step with MRoPE positions - as qsa_decode_build_index_topk,
+ * for tokens with 3-D rotary positions.  [QSA section: a block's key is rotated by the
+ * multimodal rotary position of its first token.]
+ *
+ * The call has the effect of qsa_build_index_keys_mrope (same new_mpos, pair_axis and
+ * ring_mpos; cu_new = 0, 1, .., batch; len_before = pos) followed by qsa_index_topk,
+ * and writes the same bits as those two calls.  A block completed by the new token has
+ * its first token in ring slot 0, so its angle comes from ring_mpos slot 0.
+ *
+ *   new_mpos   [batch, 3] int32   3-D position of each request's new token
+ *   pair_axis  [64] uint8 (host)  as for qsa_build_index_keys_mrope
+ *   ring_mpos  [batch, 4, 3] int32 in/out, beside ring
+ * The other arguments are those of qsa_decode_build_index_topk.  NULL new_mpos,
+ * pair_axis or ring_mpos returns QSA_E_NULL; an axis above 2 returns QSA_E_SHAPE.
+ */
+int qsa_decode_build_index_topk_mrope(const qsa_dims* dims, int32_t batch,
+                                      const uint16_t* new_idx_k, const int32_t* new_mpos,
+                                      const int32_t* pos, int32_t max_pos,
+                                      const int32_t* page_table, int32_t pt_stride,
+                                      const uint8_t* pair_axis, uint16_t* ring, int32_t* ring_mpos,
+                                      uint16_t* comp_cache, const uint16_t* idx_q,
+                                      const float* idx_w, int32_t* sel_blocks, int32_t* sel_pos,
+                                      int32_t sel_stride, int32_t* sel_count, void* workspace,
+                                      size_t ws_bytes, void* stream);
 
 /* Stage 3 - sparse GQA, decode (one query per request).  [QSA section: attention
  * weights and the weighted value sum come from the full-resolution K/V; IndexShare

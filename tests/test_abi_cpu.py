@@ -119,6 +119,25 @@ def test_decode_build_index_topk_validation():
     assert _fused(dims=bad) == B.QSA_E_UNSUPPORTED
 
 
+def test_decode_build_index_topk_mrope_validation():
+    d = B.default_dims()
+    L = B.lib()
+    axis = (ctypes.c_uint8 * 64)(*([0] * 64))
+    bad_axis = (ctypes.c_uint8 * 64)(*([0] * 63 + [3]))
+
+    def call(new_mpos=FAKE, axis_ptr=ctypes.addressof(axis), ring_mpos=FAKE, new=FAKE, batch=2):
+        return L.qsa_decode_build_index_topk_mrope(
+            ctypes.byref(d), batch, new, new_mpos, FAKE, 4096, FAKE, 64, axis_ptr, FAKE, ring_mpos, FAKE,
+            FAKE, FAKE, FAKE, FAKE, 2052, FAKE, FAKE, 1 << 30, None)
+    assert call(new_mpos=None) == B.QSA_E_NULL
+    assert call(axis_ptr=None) == B.QSA_E_NULL
+    assert call(ring_mpos=None) == B.QSA_E_NULL
+    assert call(axis_ptr=ctypes.addressof(bad_axis)) == B.QSA_E_SHAPE
+    assert call(new_mpos=FAKE + 2) == B.QSA_E_SHAPE
+    assert call(new=None) == B.QSA_E_NULL
+    assert call(batch=0) == B.QSA_E_SHAPE
+
+
 def test_build_validation():
     d = B.default_dims()
     L = B.lib()

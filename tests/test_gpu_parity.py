@@ -513,7 +513,10 @@ def _check_fused_equals_separate(wl):
     fus.build_prefix()
     fus.build_index()
     torch.cuda.synchronize()
-    for name in ("comp", "ring", "sel_blocks", "sel_pos", "sel_count"):
+    names = ["comp", "ring", "sel_blocks", "sel_pos", "sel_count"]
+    if wl.mpos is not None:
+        names.append("ring_mpos")
+    for name in names:
         assert torch.equal(getattr(sep, name), getattr(fus, name)), f"{wl.name}: {name} differs"
     for t, (a, b) in enumerate(zip(_valid_scores(sep, wl), _valid_scores(fus, wl))):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"{wl.name}: scores of row {t}"
@@ -576,3 +579,24 @@ def test_end_to_end_fused_edges(name):
 
 def test_end_to_end_fused_full():
     _check_e2e_fused(full("decode_b32_loguniform_4k_128k"))
+
+
+# MRoPE decode through the folded call: blocks completed by the decode token whose first
+# token is a vision token, with contiguous and interleaved axis maps
+FUSED_MROPE = {
+    "mrope_decode": lambda: mrope("mrope_decode"),
+    "mrope_decode_interleaved": lambda: synth.with_mrope(
+        synth.make_workload("mrope_decode_il", "decode", 320, [780, 1028, 4, 2052, 9]),
+        [[(700, 1, 7, 11)], [(1020, 1, 2, 4)], [(0, 1, 2, 2)], [], [(2, 1, 2, 3)]],
+        pair_axis=np.arange(64) % 3),
+}
+
+
+@pytest.mark.parametrize("name", list(FUSED_MROPE))
+def test_fused_build_index_mrope(name):
+    key = "fused_mrope:" + name
+    if key not in _CACHE:
+        _CACHE[key] = FUSED_MROPE[name]()
+    wl = _CACHE[key]
+    _check_fused_equals_separate(wl)
+    _check_e2e_fused(wl)
