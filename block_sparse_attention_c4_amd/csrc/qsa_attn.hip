@@ -502,13 +502,15 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   const float scale_log2 = a.sm_scale * (a.fp8 ? a.k_scale : 1.f) * kLog2e;
   const float v_scale = a.fp8 ? a.v_scale : 1.f;
   const int nblk = a.total_q * kKVHeads * a.splits;
-  // Steps in flight per wave.  Split lists (decode: every CU holds one work group)
-  // run fastest with one: more only lengthens the gathers' queues in the memory
-  // system (decode FP8 22.0 / 22.5 / 24.2 / 25.7 us and bf16 30.7 / 32.0 us for
-  // depth 1 / 2 / 3 / 4).  Whole lists (prefill, many work groups per CU) gain a
-  // little from two (2160 against 2198 us).
-  auto kern = a.fp8 ? (a.splits > 1 ? attn_kernel<true, 1> : attn_kernel<true, 2>)
-                    : (a.splits > 1 ? attn_kernel<false, 1> : attn_kernel<false, 2>);
+  // Steps in flight per wave.  Launches of at most one work group per CU (decode's
+  // split lists; target verification's 128 queries) run fastest with one: more only
+  // lengthens the gathers' queues in the memory system (decode FP8 22.0 / 22.5 /
+  // 24.2 / 25.7 us and bf16 30.7 / 32.0 us for depth 1 / 2 / 3 / 4; verification
+  // 92.2 against 94.4 us for depth 1 / 2).  Prefill chunks (many work groups per CU)
+  // gain a little from two (2160 against 2198 us).
+  const bool one_step = a.splits > 1 || nblk <= 256;
+  auto kern = a.fp8 ? (one_step ? attn_kernel<true, 1> : attn_kernel<true, 2>)
+                    : (one_step ? attn_kernel<false, 1> : attn_kernel<false, 2>);
   hipLaunchKernelGGL(kern, dim3(nblk), dim3(kThreads), 0, stream, a.q, a.q_req, a.k_pool,
                      a.v_pool, a.page_table, a.pt_stride, a.page_size, a.sel_pos, a.sel_count,
                      a.sel_stride, a.extra_pos, a.n_extra, scale_log2, v_scale, a.splits, a.part,
