@@ -1,0 +1,61 @@
+"""Host logic of bench.py (no GPU): the one-GPU refusal, the algorithmic byte
+counts behind the roofline, and the rule that HBM traffic taken by the profiler is
+reported only while the kernel sources are the ones it was taken on."""
+
+import json
+import os
+import subprocess
+import sys
+import types
+
+import numpy as np
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_decode_bytes_hand_count():
+    # two requests: p = 3 completes block 0 (4 positions attended), p = 5 leaves two
+    # tokens pending (4 + 2 positions)
+    wl = types.SimpleNamespace(q_pos=np.array([3, 5]))
+    counts = np.array([4, 6])
+    got = bench.decode_bytes(wl, counts)
+    # builder: the new key in; a completing block also reads 3 ring keys and writes its
+    # compressed key, a pending token writes its ring slot
+    assert got["build"] == (256 + 3 * 256 + 256) + (256 + 256)
+    # indexer: one 256-byte compressed key per visible block, 4 x 128 bf16 query,
+    # 4 float weights, the 512-entry block list, the positions and the count
+    per_query = 1024 + 16 + 2048 + 4
+    assert got["index"] == (256 + per_query + 4 * 4) + (256 + per_query + 4 * 6)
+    # attention: K and V rows of both KV heads (2 x 2 x 256 bf16 = 2 KB) per position,
+    # the positions and count, q and out (16 x 256 bf16 each) and the 16 lse floats
+    fixed = 4 + 2 * 16 * 256 * 2 + 16 * 4
+    assert got["attend"] == (2048 * 4 + 4 * 4 + fixed) + (2048 * 6 + 4 * 6 + fixed)
+    assert got["step"] == got["build"] + got["index"] + got["attend"]
+    # FP8 pools: 1 byte per element, drafted positions add to the attended count
+    got8 = bench.decode_bytes(wl, counts, n_extra=2, kv_bytes=1)
+    assert got8["attend"] == (1024 * 6 + 4 * 6 + fixed) + (1024 * 8 + 4 * 8 + fixed)
+
+
+def test_traffic_reported_only_for_unchanged_sources(tmp_path, monkeypatch):
+    src = tmp_path / "kernel.hip"
+    src.write_text("// kernel v1\n")
+    rec = tmp_path / "traffic.json"
+    monkeypatch.setitem(bench.KERNEL_SOURCES, "attend", [str(src)])
+    monkeypatch.setattr(bench, "traffic_file", lambda workload: str(rec))
+    monkeypatch.setattr(bench, "ROOT", "/")
+    rec.write_text(json.dumps({"attend": {"bytes_per_launch": 12345,
+                                          "source_hash": bench.source_hash([str(src)])}}))
+    assert bench.load_traffic("w", "attend") == 12345
+    src.write_text("// kernel v2\n")
+    assert bench.load_traffic("w", "attend") is None
+    rec.unlink()
+    assert bench.load_traffic("w", "attend") is None
