@@ -16,7 +16,8 @@ Sources, cited by title and section:
   [AIL]  ailone.io model page on Qwen3.8-Flash-Next, its comparison of vLLM builds:
          a K/V cache in FP8 at the speed of BF16 with a larger token pool.
 
-Readings where the pages are silent or garbled (each is listed in the design doc):
+Readings where the pages are silent or garbled (the plainest reading that the rest of
+the pages supports):
   R1  The scoring formula is cut off in [QSA]; the score of block c for a query is
       s_c = sum_h w_h * max(0, q_h . k_c) over the 4 indexer heads, no 1/sqrt(d).
   R2  "normalized" is the L2 norm, floored at 1e-12 (an all-zero mean stays zero).
