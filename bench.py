@@ -348,7 +348,7 @@ def time_loop(torch, fns, graph, steps: int, warmup: int) -> float:
 
 
 def measured_ceilings(torch) -> dict:
-    """What the box reaches on plain library work, beside the published peaks the
+    """What this machine reaches on plain library work, beside the published peaks the
     roofline uses: a 1 GiB device-to-device copy (read + write bytes per second)
     and an 8192^3 bf16 matrix product (torch.mm, contiguous operands)."""
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
