@@ -27,6 +27,25 @@ def test_header_functions_are_exported():
         assert getattr(L, n) is not None
 
 
+def test_header_is_plain_c_and_cxx(tmp_path):
+    # the ABI header is for C callers: it must compile as strict C99 and as C++17
+    import shutil
+    import subprocess
+    src = tmp_path / "use_qsa.c"
+    src.write_text('#include "qsa.h"\n'
+                   "int main(void) {\n"
+                   "  qsa_dims d = {16, 2, 256, 4, 128, 64, 1.0e7f, 0.0625f};\n"
+                   "  return (int)qsa_workspace_bytes(&d, QSA_OP_INDEX_TOPK, 1, 4096, 0) & 0;\n"
+                   "}\n")
+    inc = os.path.dirname(HEADER)
+    for cc, std, lang in (("gcc", "-std=c99", "c"), ("g++", "-std=c++17", "c++")):
+        if shutil.which(cc) is None:
+            continue
+        r = subprocess.run([cc, std, "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
+                            "-x", lang, "-I", inc, str(src)], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+
+
 def test_status_strings():
     for st in range(6):
         assert B.status_string(st).startswith("QSA_")
