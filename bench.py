@@ -76,8 +76,7 @@ WORKLOADS = {
                "126976-token prefix",
         context="126976 cached + 4096 new"),
     "prefill_chunk4096_prefix126976_mrope": dict(
-        kind="prefill", source="prefill_chunk4096_prefix126976", steps=40, warmup=5, sets=2,
-        images=[[(20000, 4, 32, 32), (126976, 1, 64, 64)]],
+        kind="prefill", steps=40, warmup=5, sets=2,
         metric="QSA chunked-prefill tokens/s with MRoPE positions (the chunk is one 64 x 64 image)",
         context="126976 cached (a 4 x 32 x 32 video span inside) + 4096 new image tokens"),
     "verify_b32x4_loguniform_4k_128k": dict(
@@ -503,8 +502,6 @@ def main() -> int:
     wl = synth.FULL_SIZE[cfg.get("source", args.workload)]()
     if kv == "fp8":
         synth.with_fp8_kv(wl)
-    if cfg.get("images"):
-        synth.with_mrope(wl, cfg["images"])
     base = runner.DeviceWorkload(wl, "cuda:0", kv=kv)
     base.build_prefix()
     torch.cuda.synchronize()
@@ -628,9 +625,9 @@ def main() -> int:
     if kind in ("decode", "indexshare"):
         config["builder"] = ("folded into the indexer call (qsa_decode_build_index_topk)" if fused
                              else "its own call (qsa_build_index_keys)")
-    if cfg.get("images"):
+    if getattr(wl, "mpos", None) is not None:
         config["rope"] = "mrope, contiguous sections 16/24/24 of the 64 indexer pairs"
-        config["vision_spans"] = [list(map(list, spans)) for spans in cfg["images"]]
+        config["vision_spans"] = [list(map(list, spans)) for spans in synth.PREFILL_MROPE_SPANS]
     result = {"metric": cfg["metric"], "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": steps,
               "warmup": warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
               "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": config}

@@ -38,7 +38,7 @@ class DeviceWorkload:
         self.dims = B.default_dims(wl.page_size, wl.rope_theta)
         self.batch = wl.batch
         self.T = wl.total_q
-        self.page_table = _i32(np.maximum(wl.page_table, 0), dev)
+        self.page_table = _i32(wl.page_table, dev)   # -1 past each request's pages
         self.pt_stride = int(wl.page_table.shape[1])
         nslots = wl.num_pages * wl.page_size
         if upload_pools and kv == "fp8":

@@ -337,6 +337,19 @@ def indexshare_b4_l262140(seed: int = 1005) -> Workload:
                          page_order="shuffled", reuse_steps=3)
 
 
+# the MRoPE prefill chunk: a 4 x 32 x 32 video span at index 20000 of the prefix, and
+# the 4096-token chunk one 64 x 64 image
+PREFILL_MROPE_SPANS = [[(20000, 4, 32, 32), (126976, 1, 64, 64)]]
+
+
+def prefill_4096_on_126976_mrope(seed: int = 1004) -> Workload:
+    """The prefill chunk with MRoPE positions (PREFILL_MROPE_SPANS, contiguous 16/24/24
+    axis map)."""
+    wl = prefill_4096_on_126976(seed)
+    wl.name = "prefill_chunk4096_prefix126976_mrope"
+    return with_mrope(wl, PREFILL_MROPE_SPANS)
+
+
 def decode_b8_l131072(seed: int = 1007) -> Workload:
     """Batch 8 at exactly L = 131072 (32768 complete blocks, no pending token): the
     literal 128K decode point, shuffled pages."""
@@ -359,4 +372,5 @@ FULL_SIZE = {
     "indexshare_b4_l262140": indexshare_b4_l262140,
     "verify_b32x4_loguniform_4k_128k": verify_b32_loguniform,
     "decode_b8_l131072": decode_b8_l131072,
+    "prefill_chunk4096_prefix126976_mrope": prefill_4096_on_126976_mrope,
 }

@@ -224,6 +224,20 @@ def score_blocks(idx_q_bits, idx_w, comp_bits) -> np.ndarray:
     return np.maximum(dots, 0.0) @ w
 
 
+def score_blocks_many(idx_q_bits, idx_w, comp_bits) -> np.ndarray:
+    """score_blocks for several queries against the same keys (reading R1):
+    row t, column c holds sum_h w[t,h] * max(0, q[t,h] . k_c).
+
+    idx_q_bits: [T, 4, d]; idx_w: [T, 4]; comp_bits: [n, d] -> [T, n] float64.
+    """
+    qh = bf16_to_f64(idx_q_bits)                  # [T, 4, d]
+    k = bf16_to_f64(comp_bits)                    # [n, d]
+    w = np.asarray(idx_w, dtype=np.float64)       # [T, 4]
+    T, H, d = qh.shape
+    dots = (qh.reshape(T * H, d) @ k.T).reshape(T, H, -1)   # [T, 4, n]
+    return np.einsum("th,thn->tn", w, np.maximum(dots, 0.0))
+
+
 def select_blocks(scores, topk: int = TOPK_BLOCKS) -> np.ndarray:
     """The best `topk` blocks [QSA], ties by lower index (R6), in ascending order."""
     s = np.asarray(scores, dtype=np.float64)
@@ -337,12 +351,6 @@ def index_state(wl, b: int, length: int):
     return build_index_state(wl.raw_idx_k[b], length, wl.rope_theta, mpos[b], wl.pair_axis)
 
 
-def comp_cache_entries(wl, b: int, comp_bits):
-    """(slots, keys) of a request's compressed keys in the compressed cache layout."""
-    c = np.arange(comp_bits.shape[0])
-    return comp_slot(wl.page_table[b], c, wl.page_size), comp_bits
-
-
 def kv_pools(wl, kv: str):
     """The workload's K/V pools and scales for kv = "bf16" or "fp8" (R9)."""
     if kv == "fp8":
@@ -369,6 +377,30 @@ def run_queries(wl, rows=None, sm_scale: float = 1.0 / 16.0, topk: int = TOPK_BL
             comp_of[b], _ = index_state(wl, b, int(wl.lengths[b]))
         res[t] = query(comp_of[b], wl.idx_q[t], wl.idx_w[t], wl.q[t], p, wl.page_table[b],
                        k_pool, v_pool, wl.page_size, sm_scale, topk, scales)
+    return res
+
+
+def run_selections(wl, rows=None, chunk: int = 256):
+    """Indexer results (scores, sel_blocks, positions) of every (or the listed) query
+    row, without attention: the rows of a request are scored against its keys in
+    batches of `chunk` queries (score_blocks_many), then selected and expanded one
+    by one."""
+    rows = list(range(wl.total_q)) if rows is None else list(rows)
+    res = {}
+    by_req = {}
+    for t in rows:
+        by_req.setdefault(int(wl.q_req[t]), []).append(t)
+    for b, ts in by_req.items():
+        comp, _ = index_state(wl, b, int(wl.lengths[b]))
+        for i in range(0, len(ts), chunk):
+            part = ts[i:i + chunk]
+            n_max = max(visible_blocks(int(wl.q_pos[t])) for t in part)
+            s_all = score_blocks_many(wl.idx_q[part], wl.idx_w[part], comp[:n_max])
+            for j, t in enumerate(part):
+                p = int(wl.q_pos[t])
+                s = s_all[j, :visible_blocks(p)].copy()
+                sel = select_blocks(s)
+                res[t] = {"scores": s, "sel_blocks": sel, "positions": expand_positions(sel, p)}
     return res
 
 

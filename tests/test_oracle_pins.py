@@ -199,6 +199,40 @@ def test_scores_brute_force_tiny():
         assert s[c] == pytest.approx(tot, rel=1e-13, abs=1e-13)
 
 
+def test_scores_many_queries_brute_force_tiny():
+    # several queries, each with its own heads and weights, against shared keys: row t
+    # must use query t's heads and weights (a swapped or transposed operand fails)
+    rng = np.random.default_rng(9)
+    T, n = 3, 5
+    q = bits(rng.standard_normal((T, 4, 128)))
+    k = bits(rng.standard_normal((n, 128)))
+    w = rng.uniform(0.5, 1.5, (T, 4)).astype(np.float32)
+    w[1] = [1.0, 0.0, 0.0, 0.0]        # one head alone: ReLU of one dot product
+    s = O.score_blocks_many(q, w, k)
+    assert s.shape == (T, n)
+    qf, kf = O.bf16_to_f64(q), O.bf16_to_f64(k)
+    for t in range(T):
+        for c in range(n):
+            tot = 0.0
+            for h in range(4):
+                dot = math.fsum(qf[t, h, i] * kf[c, i] for i in range(128))
+                tot += float(w[t, h]) * (dot if dot > 0 else 0.0)
+            assert s[t, c] == pytest.approx(tot, rel=1e-13, abs=1e-13)
+
+
+def test_selection_driver_matches_whole_queries():
+    # the indexer-only driver gives the rows' scores, selections and positions of the
+    # full per-query path (rows of two requests, a ragged last batch of rows)
+    wl = synth.make_workload("seldrv", "prefill", 26, [2300, 5000], chunk=7)
+    rows = [0, 3, 6, 7, 9, 13]
+    full = O.run_queries(wl, rows)
+    sel = O.run_selections(wl, rows, chunk=4)
+    for t in rows:
+        np.testing.assert_array_equal(sel[t]["sel_blocks"], full[t]["sel_blocks"])
+        np.testing.assert_array_equal(sel[t]["positions"], full[t]["positions"])
+        np.testing.assert_allclose(sel[t]["scores"], full[t]["scores"], rtol=1e-13, atol=1e-13)
+
+
 def test_select_all_when_few_blocks():
     for n in [0, 1, 511, 512]:
         np.testing.assert_array_equal(O.select_blocks(np.random.rand(n)), np.arange(n))
