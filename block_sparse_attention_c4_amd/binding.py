@@ -35,7 +35,7 @@ QSA_MAX_EXTRA = 8
 EXPORTED = ["qsa_status_string", "qsa_workspace_bytes", "qsa_build_index_keys", "qsa_index_topk",
             "qsa_sparse_gqa_decode", "qsa_sparse_gqa_prefill", "qsa_sparse_gqa_decode_fp8",
             "qsa_sparse_gqa_prefill_fp8", "qsa_build_index_keys_mrope", "qsa_decode_build_index_topk",
-            "qsa_decode_build_index_topk_mrope"]
+            "qsa_decode_build_index_topk_mrope", "qsa_profile_kernel_events"]
 
 
 class QsaError(RuntimeError):
@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.qsa_status_string.restype = ctypes.c_char_p
         L.qsa_status_string.argtypes = [ctypes.c_int]
+        L.qsa_profile_kernel_events.restype = ctypes.c_int
+        L.qsa_profile_kernel_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), _I]
         L.qsa_workspace_bytes.restype = _SZ
         L.qsa_workspace_bytes.argtypes = [ctypes.POINTER(QsaDims), ctypes.c_int, _I, _I, _I]
         L.qsa_build_index_keys.restype = ctypes.c_int
@@ -133,6 +135,14 @@ def _stream(stream) -> int | None:
 def _check(status: int, where: str) -> None:
     if status != QSA_OK:
         raise QsaError(status, where)
+
+
+def qsa_profile_kernel_events(events) -> None:
+    """events: torch.cuda.Event objects (or raw hipEvent_t handles) that the calling
+    thread's next QSA call records after its first len(events) kernels."""
+    handles = [e.cuda_event if hasattr(e, "cuda_event") else int(e) for e in events]
+    arr = (ctypes.c_void_p * max(len(handles), 1))(*handles)
+    _check(lib().qsa_profile_kernel_events(arr, len(handles)), "qsa_profile_kernel_events")
 
 
 def qsa_workspace_bytes(dims: QsaDims, op: int, total_q: int, max_pos: int = 0, n_extra: int = 0) -> int:

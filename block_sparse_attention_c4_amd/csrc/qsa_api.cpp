@@ -26,7 +26,27 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int hip_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_E_HIP; }
 
+// HIP events that the calling thread asked the next call to record after its
+// kernels (qsa_profile_kernel_events).  A call's CallScope drops the request when
+// the call returns, whether or not every event was recorded.
+constexpr int kMaxProfileEvents = 8;
+struct ProfileEvents {
+  hipEvent_t ev[kMaxProfileEvents];
+  int n = 0, next = 0;
+};
+thread_local ProfileEvents t_profile;
+
+struct CallScope {
+  ~CallScope() { t_profile.n = t_profile.next = 0; }
+};
+
 }  // namespace
+
+namespace qsa {
+void note_launch(hipStream_t stream) {
+  if (t_profile.next < t_profile.n) hipEventRecord(t_profile.ev[t_profile.next++], stream);
+}
+}  // namespace qsa
 
 extern "C" {
 
@@ -40,6 +60,18 @@ const char* qsa_status_string(int status) {
     case QSA_E_HIP: return "QSA_E_HIP: a HIP launch failed";
     default: return "QSA: unknown status";
   }
+}
+
+int qsa_profile_kernel_events(void* const* events, int32_t n_events) {
+  if (n_events < 0 || n_events > kMaxProfileEvents) return QSA_E_SHAPE;
+  if (n_events > 0 && !events) return QSA_E_NULL;
+  for (int i = 0; i < n_events; ++i) {
+    if (!events[i]) return QSA_E_NULL;
+    t_profile.ev[i] = static_cast<hipEvent_t>(events[i]);
+  }
+  t_profile.n = n_events;
+  t_profile.next = 0;
+  return QSA_OK;
 }
 
 size_t qsa_workspace_bytes(const qsa_dims* dims, int op, int32_t total_q, int32_t max_pos,
@@ -92,6 +124,7 @@ static int build_common(const qsa_dims* dims, int32_t batch, const uint16_t* new
                         int32_t total_new, int32_t max_new, const int32_t* page_table,
                         int32_t pt_stride, const uint8_t* pair_axis, uint16_t* ring,
                         int32_t* ring_mpos, uint16_t* comp_cache, void* stream) {
+  CallScope scope;
   int st = check_dims(dims);
   if (st != QSA_OK) return st;
   if (batch < 0 || total_new < 0 || max_new < 0 || max_new > total_new || pt_stride < 1 ||
@@ -125,6 +158,7 @@ int qsa_index_topk(const qsa_dims* dims, int32_t batch, int32_t total_q, const u
                    const uint16_t* comp_cache, int32_t* sel_blocks, int32_t* sel_pos,
                    int32_t sel_stride, int32_t* sel_count, void* workspace, size_t ws_bytes,
                    void* stream) {
+  CallScope scope;
   int st = check_dims(dims);
   if (st != QSA_OK) return st;
   if (batch < 1 || total_q < 0 || max_pos < 1 || max_pos > QSA_MAX_CONTEXT || pt_stride < 1 ||
@@ -167,6 +201,7 @@ static int decode_build_index_common(const qsa_dims* dims, int32_t batch,
                                      const float* idx_w, int32_t* sel_blocks, int32_t* sel_pos,
                                      int32_t sel_stride, int32_t* sel_count, void* workspace,
                                      size_t ws_bytes, void* stream) {
+  CallScope scope;
   int st = check_dims(dims);
   if (st != QSA_OK) return st;
   if (batch < 1 || batch > 65535 || max_pos < 1 || max_pos > QSA_MAX_CONTEXT || pt_stride < 1 ||
@@ -246,6 +281,7 @@ static int gqa_common(const qsa_dims* dims, int32_t total_q, const uint16_t* q,
                       const int32_t* sel_pos, const int32_t* sel_count, int32_t sel_stride,
                       const int32_t* extra_pos, int32_t n_extra, uint16_t* out, float* lse,
                       void* workspace, size_t ws_bytes, void* stream) {
+  CallScope scope;
   int st = check_dims(dims);
   if (st != QSA_OK) return st;
   if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))

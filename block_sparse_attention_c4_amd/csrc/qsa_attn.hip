@@ -281,7 +281,7 @@ attn_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ q_req,
   const int span = min(((sp + 1) * nchunk / splits) * kChunk, bound) - start;
   const int req = q_req ? q_req[t] : t;
   const int cnt = sel_count[t];
-  QSA_CHECK(cnt >= 0 && cnt <= sel_stride);
+  QSA_CHECK(cnt >= 0 && cnt <= sel_stride && cnt <= kMaxSel);   // the splits cover kMaxSel + n_extra
   const int total = cnt + n_extra;
   const int len = max(0, min(span, total - start));
   // Translate the positions to pool slots (-1 = no position).  All list loads
@@ -515,9 +515,11 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
                      a.v_pool, a.page_table, a.pt_stride, a.page_size, a.sel_pos, a.sel_count,
                      a.sel_stride, a.extra_pos, a.n_extra, scale_log2, v_scale, a.splits, a.part,
                      a.out, a.lse);
+  note_launch(stream);
   if (a.splits > 1) {
     hipLaunchKernelGGL(combine_kernel, dim3(a.total_q * kKVHeads), dim3(256), 0, stream, a.part,
                        a.splits, v_scale, a.out, a.lse);
+    note_launch(stream);
   }
   return hipGetLastError();
 }

@@ -116,6 +116,7 @@ hipError_t launch_build(const BuildArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(build_kernel, grid, dim3(64), 0, stream, a.new_k, a.cu_new, a.len_before,
                      a.page_table, a.pt_stride, a.page_size, a.ring, a.comp, a.new_mpos,
                      a.ring_mpos, rope);
+  note_launch(stream);
   return hipGetLastError();
 }
 

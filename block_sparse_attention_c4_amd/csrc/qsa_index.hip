@@ -579,6 +579,7 @@ hipError_t launch_index(const IndexArgs& a, hipStream_t stream) {
                          a.page_table, a.pt_stride, a.page_size, a.comp,
                          a.scores + (size_t)q0 * a.score_stride, a.score_stride,
                          a.gmax_f + (size_t)q0 * (a.score_stride / kScoreGroup));
+      note_launch(stream);
     }
     launch_topk(a, stream);
     return hipGetLastError();
@@ -600,6 +601,7 @@ hipError_t launch_index(const IndexArgs& a, hipStream_t stream) {
                        a.q_req + q0, a.q_pos + q0, a.page_table, a.pt_stride, a.page_size, a.comp,
                        a.scores + (size_t)q0 * a.score_stride, a.score_stride,
                        a.gmax_f + (size_t)q0 * (a.score_stride / kScoreGroup));
+    note_launch(stream);
   }
   launch_topk(a, stream);
   return hipGetLastError();
@@ -634,6 +636,7 @@ hipError_t launch_index_ingest(const IndexArgs& a, const IngestArgs& f, hipStrea
                        a.q_pos + q0, a.page_table, a.pt_stride, a.page_size, a.comp,
                        a.scores + (size_t)q0 * a.score_stride, a.score_stride,
                        a.gmax_f + (size_t)q0 * (a.score_stride / kScoreGroup), ing);
+    note_launch(stream);
   }
   launch_topk(a, stream);
   return hipGetLastError();

@@ -7,6 +7,10 @@
 
 namespace qsa {
 
+// Called after every kernel launch: records the next of the HIP events that the
+// calling thread asked for with qsa_profile_kernel_events, if any are left.
+void note_launch(hipStream_t stream);
+
 struct RopeTable {
   double inv_freq[64];   // theta^(-2i/128), i < 64
   uint8_t axis[64];      // MRoPE: position component (0 t, 1 h, 2 w) that turns pair i

@@ -558,12 +558,14 @@ topk_queued_kernel(const int* __restrict__ queue, const float* __restrict__ scor
 void launch_topk(const IndexArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(topk_kernel, dim3(a.total_q), dim3(kT), 0, stream, a.scores, a.score_stride,
                      a.gmax_f, a.q_pos, a.sel_blocks, a.sel_pos, a.sel_stride, a.sel_count);
+  note_launch(stream);
 }
 
 void launch_topk_queued(const IndexArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(topk_queued_kernel, dim3(std::min(a.total_q, 256)), dim3(kT), 0, stream, a.queue,
                      a.scores, a.score_stride, a.q_pos, a.sel_blocks, a.sel_pos, a.sel_stride,
                      a.sel_count);
+  note_launch(stream);
 }
 
 }  // namespace qsa

@@ -88,6 +88,21 @@ enum qsa_op {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* qsa_status_string(int status);
 
+/* Profiling aid: the calling thread's next QSA call (any entry point below)
+ * records events[i] on its stream right after launching its i-th kernel, for i <
+ * n_events and as many kernels as it launches; then the request lapses.  With it a
+ * caller times each kernel of a multi-kernel call with HIP events (event i minus
+ * event i-1, or minus an event recorded before the call).  events: n_events
+ * hipEvent_t handles created by the caller (host array).  n_events in 0..8 (0
+ * cancels), else QSA_E_SHAPE; a NULL handle gives QSA_E_NULL.  It changes no
+ * result.  The kernels a call launches, in order: qsa_decode_build_index_topk: the
+ * scorer (builder folded in), then the select; qsa_index_topk: the scorer (one
+ * launch per 64 queries, or per 256 queries of the multi-query scorer, in decode
+ * and verification batches), then the select, and for prefill chunks the MFMA
+ * scorer, the code select, the exact rescoring and the queued select; the sparse
+ * GQA calls: the gather, then the split combine when the list is split. */
+int qsa_profile_kernel_events(void* const* events, int32_t n_events);
+
 /* Workspace bytes that `op` needs for `total_q` queries.
  *   INDEX_TOPK:  max_pos = an upper bound on every q_pos + 1 (host).
  *   GQA_DECODE / GQA_PREFILL: n_extra = columns of extra_pos (0 for prefill).
@@ -260,7 +275,10 @@ int qsa_decode_build_index_topk_mrope(const qsa_dims* dims, int32_t batch,
  *
  *   q          [batch, Hq, D] bf16
  *   k_pool, v_pool [slots, Hkv, D] bf16
- *   sel_pos [batch, sel_stride], sel_count [batch] int32 (sel_count <= sel_stride)
+ *   sel_pos [batch, sel_stride], sel_count [batch] int32; sel_count <= sel_stride
+ *              and sel_count <= QSA_MAX_SEL (the most an indexer row can hold; the
+ *              kernels size their per-query work for it, and the QSA_DEBUG build
+ *              traps on a larger count)
  *   extra_pos  [batch, n_extra] int32 or NULL (n_extra = 0); n_extra <= QSA_MAX_EXTRA
  *   out        [batch, Hq, D] bf16 out;  lse [batch, Hq] float out or NULL
  *   workspace  >= qsa_workspace_bytes(QSA_OP_GQA_DECODE, batch, 0, n_extra)
@@ -277,6 +295,7 @@ int qsa_sparse_gqa_decode(const qsa_dims* dims, int32_t batch, const uint16_t* q
  * prefill the expanded indices feed sparse GQA.]
  *
  *   q [total_q, Hq, D] bf16;  q_req [total_q] int32;  out [total_q, Hq, D] bf16;
+ *   sel_count [total_q] <= min(sel_stride, QSA_MAX_SEL), as for the decode call;
  *   lse [total_q, Hq] float or NULL;
  *   workspace >= qsa_workspace_bytes(QSA_OP_GQA_PREFILL, total_q, 0, 0)
  */

@@ -196,6 +196,23 @@ def test_gqa_validation():
                                     2052, FAKE, None, None, 0, None) == B.QSA_E_NULL   # q_req missing
 
 
+def test_profile_kernel_events_validation():
+    L = B.lib()
+    ev = (ctypes.c_void_p * 9)(*([FAKE] * 9))
+    assert L.qsa_profile_kernel_events(ev, 9) == B.QSA_E_SHAPE
+    assert L.qsa_profile_kernel_events(ev, -1) == B.QSA_E_SHAPE
+    assert L.qsa_profile_kernel_events(None, 2) == B.QSA_E_NULL
+    ev[1] = None
+    assert L.qsa_profile_kernel_events(ev, 2) == B.QSA_E_NULL
+    assert L.qsa_profile_kernel_events(None, 0) == B.QSA_OK        # cancels
+    # a request lapses with the next call, even one that fails validation and records
+    # nothing (otherwise a later call would record into events the caller dropped)
+    assert L.qsa_profile_kernel_events(ev, 1) == B.QSA_OK
+    d = B.default_dims()
+    assert L.qsa_sparse_gqa_decode(ctypes.byref(d), 8, None, FAKE, FAKE, FAKE, 64, FAKE, FAKE, 2052,
+                                   None, 0, FAKE, None, FAKE, 1 << 30, None) == B.QSA_E_NULL
+
+
 def test_gqa_fp8_validation():
     d = B.default_dims()
     L = B.lib()
