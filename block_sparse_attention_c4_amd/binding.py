@@ -21,6 +21,7 @@ QSA_E_SHAPE = 2
 QSA_E_UNSUPPORTED = 3
 QSA_E_WORKSPACE = 4
 QSA_E_HIP = 5
+QSA_E_SCRATCH = 6
 
 QSA_OP_INDEX_TOPK = 1
 QSA_OP_GQA_DECODE = 2
@@ -31,11 +32,13 @@ QSA_TOPK = 512
 QSA_MAX_SEL = 2051
 QSA_MAX_CONTEXT = 262144
 QSA_MAX_EXTRA = 8
+QSA_ATTN_SCRATCH_BYTES = 8 << 20
 
 EXPORTED = ["qsa_status_string", "qsa_workspace_bytes", "qsa_build_index_keys", "qsa_index_topk",
             "qsa_sparse_gqa_decode", "qsa_sparse_gqa_prefill", "qsa_sparse_gqa_decode_fp8",
             "qsa_sparse_gqa_prefill_fp8", "qsa_build_index_keys_mrope", "qsa_decode_build_index_topk",
-            "qsa_decode_build_index_topk_mrope", "qsa_profile_kernel_events"]
+            "qsa_decode_build_index_topk_mrope", "qsa_sparse_gqa_decode_noalloc",
+            "qsa_profile_kernel_events"]
 
 
 class QsaError(RuntimeError):
@@ -84,6 +87,9 @@ def lib() -> ctypes.CDLL:
         L.qsa_sparse_gqa_decode.restype = ctypes.c_int
         L.qsa_sparse_gqa_decode.argtypes = [ctypes.POINTER(QsaDims), _I, _P, _P, _P, _P, _I, _P, _P,
                                             _I, _P, _I, _P, _P, _P, _SZ, _P]
+        L.qsa_sparse_gqa_decode_noalloc.restype = ctypes.c_int
+        L.qsa_sparse_gqa_decode_noalloc.argtypes = [ctypes.POINTER(QsaDims), _I, _P, _P, _P, _P, _I,
+                                                    _P, _P, _I, _P, _I, _P, _P, _P]
         L.qsa_sparse_gqa_prefill.restype = ctypes.c_int
         L.qsa_sparse_gqa_prefill.argtypes = [ctypes.POINTER(QsaDims), _I, _P, _P, _P, _P, _P, _I, _P,
                                              _P, _I, _P, _P, _P, _SZ, _P]
@@ -200,6 +206,16 @@ def qsa_sparse_gqa_decode(dims, batch, q, k_pool, v_pool, page_table, pt_stride,
                                      sel_stride, _ptr(extra_pos), n_extra, _ptr(out), _ptr(lse),
                                      _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "qsa_sparse_gqa_decode")
+
+
+def qsa_sparse_gqa_decode_noalloc(dims, batch, q, k_pool, v_pool, page_table, pt_stride, sel_pos,
+                                  sel_count, sel_stride, extra_pos, n_extra, out, lse,
+                                  stream=None) -> None:
+    st = lib().qsa_sparse_gqa_decode_noalloc(ctypes.byref(dims), batch, _ptr(q), _ptr(k_pool),
+                                             _ptr(v_pool), _ptr(page_table), pt_stride, _ptr(sel_pos),
+                                             _ptr(sel_count), sel_stride, _ptr(extra_pos), n_extra,
+                                             _ptr(out), _ptr(lse), _stream(stream))
+    _check(st, "qsa_sparse_gqa_decode_noalloc")
 
 
 def qsa_sparse_gqa_prefill(dims, total_q, q, q_req, k_pool, v_pool, page_table, pt_stride, sel_pos,

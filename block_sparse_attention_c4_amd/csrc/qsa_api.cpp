@@ -9,6 +9,8 @@
 
 #include "qsa_launch.h"
 
+static_assert(qsa::kAttnScratchBytes == QSA_ATTN_SCRATCH_BYTES, "scratch size as declared in qsa.h");
+
 namespace {
 
 bool dims_supported(const qsa_dims* d) {
@@ -58,6 +60,8 @@ const char* qsa_status_string(int status) {
     case QSA_E_UNSUPPORTED: return "QSA_E_UNSUPPORTED: dims other than 16/2/256 heads, 4x128 indexer";
     case QSA_E_WORKSPACE: return "QSA_E_WORKSPACE: workspace missing, misaligned or too small";
     case QSA_E_HIP: return "QSA_E_HIP: a HIP launch failed";
+    case QSA_E_SCRATCH:
+      return "QSA_E_SCRATCH: the call needs more scratch than the library's static buffer holds";
     default: return "QSA: unknown status";
   }
 }
@@ -275,12 +279,15 @@ int qsa_decode_build_index_topk_mrope(const qsa_dims* dims, int32_t batch,
 }
 
 // fp8: the pools hold E4M3 codes scaled by k_scale / v_scale (finite and > 0).
+// static_scratch: the split partials go to the library's static device array instead
+// of the caller's workspace (workspace and ws_bytes are ignored).
 static int gqa_common(const qsa_dims* dims, int32_t total_q, const uint16_t* q,
                       const int32_t* q_req, const void* k_pool, const void* v_pool, bool fp8,
                       float k_scale, float v_scale, const int32_t* page_table, int32_t pt_stride,
                       const int32_t* sel_pos, const int32_t* sel_count, int32_t sel_stride,
                       const int32_t* extra_pos, int32_t n_extra, uint16_t* out, float* lse,
-                      void* workspace, size_t ws_bytes, void* stream) {
+                      void* workspace, size_t ws_bytes, void* stream,
+                      bool static_scratch = false) {
   CallScope scope;
   int st = check_dims(dims);
   if (st != QSA_OK) return st;
@@ -295,8 +302,13 @@ static int gqa_common(const qsa_dims* dims, int32_t total_q, const uint16_t* q,
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16))
     return QSA_E_SHAPE;
   const size_t need = qsa::attn_workspace_bytes(total_q, n_extra);
-  if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 256)))
+  if (static_scratch) {
+    if (need > qsa::kAttnScratchBytes) return QSA_E_SCRATCH;
+    workspace = nullptr;
+    if (need > 0 && qsa::attn_scratch(&workspace) != hipSuccess) return QSA_E_HIP;
+  } else if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 256))) {
     return QSA_E_WORKSPACE;
+  }
   qsa::AttnArgs a;
   a.total_q = total_q;
   a.page_size = dims->page_size;
@@ -331,6 +343,17 @@ int qsa_sparse_gqa_decode(const qsa_dims* dims, int32_t batch, const uint16_t* q
   return gqa_common(dims, batch, q, nullptr, k_pool, v_pool, false, 1.f, 1.f, page_table,
                     pt_stride, sel_pos, sel_count, sel_stride, extra_pos, n_extra, out, lse,
                     workspace, ws_bytes, stream);
+}
+
+int qsa_sparse_gqa_decode_noalloc(const qsa_dims* dims, int32_t batch, const uint16_t* q,
+                                  const uint16_t* k_pool, const uint16_t* v_pool,
+                                  const int32_t* page_table, int32_t pt_stride,
+                                  const int32_t* sel_pos, const int32_t* sel_count,
+                                  int32_t sel_stride, const int32_t* extra_pos, int32_t n_extra,
+                                  uint16_t* out, float* lse, void* stream) {
+  return gqa_common(dims, batch, q, nullptr, k_pool, v_pool, false, 1.f, 1.f, page_table,
+                    pt_stride, sel_pos, sel_count, sel_stride, extra_pos, n_extra, out, lse,
+                    nullptr, 0, stream, true);
 }
 
 int qsa_sparse_gqa_decode_fp8(const qsa_dims* dims, int32_t batch, const uint16_t* q,

@@ -33,6 +33,8 @@
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
+#include <atomic>
+
 namespace qsa {
 
 namespace {
@@ -494,6 +496,32 @@ size_t attn_workspace_bytes(int total_q, int n_extra) {
   attn_plan(total_q, n_extra, &splits, &len);
   if (splits == 1) return 0;
   return (size_t)total_q * kKVHeads * splits * kPartFloats * sizeof(float);
+}
+
+// Scratch of the allocation-free decode call (qsa_sparse_gqa_decode_noalloc): the
+// split partials live in this file-scope device array instead of a caller
+// workspace.  Every GPU that runs the library holds its own copy until the process
+// ends.  In host code `scratch` names only a host-side stand-in; its device address
+// on the current GPU comes from hipGetSymbolAddress, taken once per device and kept
+// in scratch_ptr[].  Calls that overlap on one GPU share (and race on) the array.
+static __device__ __align__(256) float scratch[kAttnScratchBytes / sizeof(float)];
+
+constexpr int kScratchDevices = 64;
+static std::atomic<void*> scratch_ptr[kScratchDevices];
+
+hipError_t attn_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+    scratch_ptr[dev].store(p, std::memory_order_release);   // racing threads store the same address
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {

@@ -91,6 +91,10 @@ struct AttnArgs {
 };
 void attn_plan(int total_q, int n_extra, int* splits, int* split_len);
 size_t attn_workspace_bytes(int total_q, int n_extra);
+// Static scratch of the allocation-free decode call: its size, and its device
+// address on the current GPU (looked up once per device).
+constexpr size_t kAttnScratchBytes = size_t(8) << 20;
+hipError_t attn_scratch(void** ptr);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace qsa

@@ -15,7 +15,8 @@
  *  - Pointers are DEVICE pointers unless marked "host".  The caller owns every
  *    buffer; the library never allocates, frees or synchronises, and reads no
  *    device memory back to the host.  Scratch memory comes from the caller's
- *    workspace, sized by qsa_workspace_bytes().
+ *    workspace, sized by qsa_workspace_bytes() (qsa_sparse_gqa_decode_noalloc
+ *    uses the library's static device array instead).
  *  - bf16 tensors are passed as uint16_t bit patterns; all are row-major and
  *    densely packed in the shapes given.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
@@ -27,7 +28,8 @@
  *    in the ranges stated below.  The library built with -DQSA_DEBUG
  *    (libqsa_debug.so) checks them where the kernels read them and traps the
  *    kernel on a violation.
- *  - Reentrant; no mutable global state.
+ *  - Reentrant; no mutable global state, except that qsa_sparse_gqa_decode_noalloc
+ *    keeps a static scratch array on each device and caches its address.
  *
  * Supported shapes: num_q_heads = 16, num_kv_heads = 2, head_dim = 256,
  * idx_heads = 4, idx_dim = 128, page_size a multiple of 16 (64 in practice),
@@ -76,7 +78,8 @@ enum qsa_status {
   QSA_E_SHAPE = 2,       /* a size or stride is out of range                 */
   QSA_E_UNSUPPORTED = 3, /* dims other than the compiled ones                */
   QSA_E_WORKSPACE = 4,   /* workspace missing or smaller than required       */
-  QSA_E_HIP = 5          /* a HIP launch failed (see hipGetLastError)        */
+  QSA_E_HIP = 5,         /* a HIP launch failed (see hipGetLastError)        */
+  QSA_E_SCRATCH = 6      /* more scratch than the static buffer holds        */
 };
 
 enum qsa_op {
@@ -289,6 +292,32 @@ int qsa_sparse_gqa_decode(const qsa_dims* dims, int32_t batch, const uint16_t* q
                           const int32_t* sel_count, int32_t sel_stride, const int32_t* extra_pos,
                           int32_t n_extra, uint16_t* out, float* lse, void* workspace,
                           size_t ws_bytes, void* stream);
+
+/* Stage 3, decode, without a workspace: qsa_sparse_gqa_decode for callers that
+ * cannot allocate device memory (code under hipGraph capture, tight serving loops
+ * such as the IndexShare draft steps, harnesses that forbid hipMalloc).
+ *
+ * Arguments and results are those of qsa_sparse_gqa_decode (same kernels, same
+ * bits), minus the workspace: the split partials go to a device array that the
+ * library holds on every GPU it runs on, QSA_ATTN_SCRATCH_BYTES bytes, until the
+ * process ends.  The call allocates nothing.  Its device address is looked up on
+ * the first call on each device, which must be the current device (the one
+ * `stream` belongs to).
+ *  - Calls on one GPU share that array: calls that may overlap (on different
+ *    streams, or from different threads) race on it and must be ordered by the
+ *    caller.  Nothing in it needs clearing: every call writes the partials it reads.
+ *  - A call needing more than QSA_ATTN_SCRATCH_BYTES returns QSA_E_SCRATCH and
+ *    enqueues nothing.  Every batch size fits today: the partials are largest near
+ *    batch 127 (4,194,048 bytes); from batch 128 on the call needs none.
+ *  - QSA_E_HIP if the array's address cannot be obtained.
+ */
+#define QSA_ATTN_SCRATCH_BYTES (8u << 20)
+int qsa_sparse_gqa_decode_noalloc(const qsa_dims* dims, int32_t batch, const uint16_t* q,
+                                  const uint16_t* k_pool, const uint16_t* v_pool,
+                                  const int32_t* page_table, int32_t pt_stride,
+                                  const int32_t* sel_pos, const int32_t* sel_count,
+                                  int32_t sel_stride, const int32_t* extra_pos, int32_t n_extra,
+                                  uint16_t* out, float* lse, void* stream);
 
 /* Stage 3 - sparse GQA over a chunk of prefill queries: as the decode call, with
  * query t reading request q_req[t] and no extra positions.  [QSA section: for

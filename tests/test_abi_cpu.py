@@ -47,7 +47,7 @@ def test_header_is_plain_c_and_cxx(tmp_path):
 
 
 def test_status_strings():
-    for st in range(6):
+    for st in range(7):
         assert B.status_string(st).startswith("QSA_")
     assert "unknown" in B.status_string(99)
 
@@ -194,6 +194,32 @@ def test_gqa_validation():
     assert dec(q=FAKE + 8) == B.QSA_E_SHAPE
     assert L.qsa_sparse_gqa_prefill(ctypes.byref(d), 4, FAKE, None, FAKE, FAKE, FAKE, 64, FAKE, FAKE,
                                     2052, FAKE, None, None, 0, None) == B.QSA_E_NULL   # q_req missing
+
+
+def test_gqa_noalloc_validation():
+    # the allocation-free decode call checks its arguments as the workspace call does,
+    # before it looks up its static scratch (which needs a GPU)
+    d = B.default_dims()
+    L = B.lib()
+
+    def dec(**k):
+        return L.qsa_sparse_gqa_decode_noalloc(ctypes.byref(d), k.get("batch", 8), k.get("q", FAKE), FAKE,
+                                               FAKE, FAKE, 64, FAKE, FAKE, 2052, k.get("extra", FAKE),
+                                               k.get("n_extra", 4), k.get("out", FAKE), None, None)
+    assert dec(batch=0) == B.QSA_OK
+    assert dec(q=None) == B.QSA_E_NULL
+    assert dec(out=None) == B.QSA_E_NULL
+    assert dec(extra=None) == B.QSA_E_NULL
+    assert dec(n_extra=9) == B.QSA_E_SHAPE
+    assert dec(q=FAKE + 8) == B.QSA_E_SHAPE
+    bad = B.default_dims()
+    bad.head_dim = 128
+    assert L.qsa_sparse_gqa_decode_noalloc(ctypes.byref(bad), 8, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE,
+                                           2052, None, 0, FAKE, None, None) == B.QSA_E_UNSUPPORTED
+    # every batch size's split partials fit the static scratch
+    need = max(B.qsa_workspace_bytes(d, B.QSA_OP_GQA_DECODE, b, 0, e)
+               for b in range(1, 300) for e in (0, 4, 8))
+    assert 0 < need <= B.QSA_ATTN_SCRATCH_BYTES
 
 
 def test_profile_kernel_events_validation():
