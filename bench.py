@@ -87,30 +87,35 @@ WORKLOADS = {
 }
 
 _CSRC = "block_sparse_attention_c4_amd/csrc/"
-KERNEL_SOURCES = {
-    "attend": [_CSRC + f for f in ("qsa_attn.hip", "qsa_device.h", "qsa_launch.h")],
-    "index": [_CSRC + f for f in ("qsa_index.hip", "qsa_topk.hip", "qsa_prefill.hip", "qsa_device.h",
-                                  "qsa_keymath.h", "qsa_launch.h")],
-    "build": [_CSRC + f for f in ("qsa_build.hip", "qsa_device.h", "qsa_keymath.h", "qsa_launch.h")],
-    "build_index": [_CSRC + f for f in ("qsa_index.hip", "qsa_topk.hip", "qsa_device.h", "qsa_keymath.h",
-                                        "qsa_launch.h")],
+_COMMON = [_CSRC + f for f in ("qsa_device.h", "qsa_launch.h")]
+_SRC_OF = {
+    "qsa_attn.hip": ["attn_kernel", "combine_kernel"],
+    "qsa_build.hip": ["build_kernel"],
+    "qsa_index.hip": ["score_kernel", "score_build_kernel", "score_multi_kernel"],
+    "qsa_topk.hip": ["topk_kernel", "topk_queued_kernel"],
+    "qsa_prefill.hip": ["score_mfma_kernel", "topk_codes_kernel", "rescore_kernel"],
 }
+# the sources each kernel is compiled from (traffic figures are kept only while they hash the same)
+KERNEL_SOURCES = {k: [_CSRC + f] + _COMMON + [_CSRC + "qsa_keymath.h"] for f, ks in _SRC_OF.items() for k in ks}
 ENTRY = {"build": "qsa_build_index_keys", "index": "qsa_index_topk", "attend": "qsa_sparse_gqa_decode",
          "build_index": "qsa_decode_build_index_topk"}
 
 
-def stage_kernels(kind: str, kv: str = "bf16", fused: bool = False) -> dict:
+def stage_kernels(kind: str, dw, fused: bool = False) -> dict:
+    """The kernels each stage's call launches, in order (stage -> list of names)."""
+    attend = ["attn_kernel"] + (["combine_kernel"] if dw.ws_attn_bytes > 0 else [])
     if kind == "verify":
-        return {"build": "build_kernel", "index": "score_multi_kernel + topk_kernel",
-                "attend": "attn_kernel + combine_kernel"}
+        return {"build": ["build_kernel"],
+                "index": ["score_multi_kernel"] * ((dw.T + 255) // 256) + ["topk_kernel"],
+                "attend": attend}
     if kind == "prefill":
-        return {"build": "build_kernel",
-                "index": "score_mfma_kernel + topk_codes_kernel (+ rescore_kernel, topk_queued_kernel)",
-                "attend": "attn_kernel + combine_kernel"}
-    attend = "attn_kernel<fp8> + combine_kernel" if kv == "fp8" else "attn_kernel + combine_kernel"
+        return {"build": ["build_kernel"],
+                "index": ["score_mfma_kernel", "topk_codes_kernel", "rescore_kernel", "topk_queued_kernel"],
+                "attend": attend}
     if fused:
-        return {"build_index": "score_build_kernel + topk_kernel", "attend": attend}
-    return {"build": "build_kernel", "index": "score_kernel + topk_kernel", "attend": attend}
+        return {"build_index": ["score_build_kernel", "topk_kernel"], "attend": attend}
+    return {"build": ["build_kernel"], "index": ["score_kernel"] * ((dw.T + 63) // 64) + ["topk_kernel"],
+            "attend": attend}
 
 
 def traffic_file(workload: str) -> str:
@@ -134,6 +139,16 @@ def decode_bytes(wl, counts: np.ndarray, n_extra: int = 0, kv_bytes: int = 2) ->
     att = counts + n_extra
     attend = int(np.sum(2 * 2 * 256 * kv_bytes * att + 4 * att + 4 + 16 * 256 * 2 * 2 + 16 * 4))
     return {"build": build, "index": index, "attend": attend, "step": build + index + attend}
+
+
+def attend_kernel_bytes(attend_bytes: int, n_queries: int, combined: bool) -> dict:
+    """The attention call's algorithmic bytes split between its kernels: the gather
+    reads K/V, positions and q; the output (16 x 256 bf16) and lse (16 floats) of each
+    query are written by the combine when the list is split, else by the gather."""
+    out = n_queries * (16 * 256 * 2 + 16 * 4)
+    if not combined:
+        return {"attn_kernel": attend_bytes}
+    return {"attn_kernel": attend_bytes - out, "combine_kernel": out}
 
 
 def verify_bytes(wl, sel_pos: np.ndarray, counts: np.ndarray) -> dict:
@@ -184,35 +199,26 @@ def source_hash(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, stage: str):
-    """HBM bytes per launch of the stage's kernels from the committed rocprofv3
-    counter runs, or None if they were taken on different kernel sources."""
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter runs, or
+    None if they were taken on different kernel sources."""
     path = traffic_file(workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    ent = rec.get(stage)
+    ent = rec.get(kernel)
     if not ent:
         return None
-    cur = source_hash([os.path.join(ROOT, p) for p in KERNEL_SOURCES[stage]])
+    cur = source_hash([os.path.join(ROOT, p) for p in KERNEL_SOURCES[kernel]])
     return ent["bytes_per_launch"] if ent.get("source_hash") == cur else None
 
 
 # ------------------------------------------------------------------ CPU baseline (oracle)
 
-def _oracle_keys_at(O, wl, b: int, prefix_keys, p: int):
-    """A request's compressed keys as a query at p sees them: the prefix keys plus
-    the block the query token completes, if it completes one."""
-    if (p + 1) % 4:
-        return prefix_keys
-    c = p // 4
-    blk = O.compress_blocks(wl.raw_idx_k[b][4 * c:4 * c + 4][None], np.array([4 * c]), wl.rope_theta)
-    return np.concatenate([prefix_keys, blk])
-
-
 def host_cpu() -> dict:
-    """The host the oracle ran on: CPU model and the processors the OS reports."""
+    """The host the oracle ran on: CPU model, the processors the OS reports and the
+    ones this process may run on."""
     model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -222,21 +228,97 @@ def host_cpu() -> dict:
                     break
     except OSError:
         pass
-    return {"cpu_model": model, "nproc": os.cpu_count()}
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity": aff}
 
 
-def cpu_baseline(wl, seconds: float, kv: str = "bf16") -> dict:
-    """The oracle on the same workload, single-threaded, for about `seconds`: decode
-    queries over the batch, prefill query rows of the chunk, or IndexShare reuse
-    steps.  The prefix keys are built untimed; for prefill the chunk's own
-    compressed keys are built inside the timed region."""
+def oracle_workers() -> int:
+    """Worker processes for the oracle: the CPUs this process may use, at most 16 (a
+    one-GPU share of the host)."""
+    return max(1, min(16, host_cpu()["affinity"]))
+
+
+# The oracle's unit of work (one decode query, one prefill query row, or one
+# IndexShare reuse step) runs in this process or in spawned workers.  Its inputs are
+# .npy files in a scratch directory (under /dev/shm when it exists), which every
+# worker maps read-only instead of receiving copies.
+_UNIT_STATE = {}
+
+
+def _unit_arrays(path: str) -> dict:
+    if _UNIT_STATE.get("_dir") != path:
+        _UNIT_STATE.clear()
+        _UNIT_STATE["_dir"] = path
+        for f in os.listdir(path):
+            if f.endswith(".npy"):
+                _UNIT_STATE[f[:-4]] = np.load(os.path.join(path, f), mmap_mode="r")
+    return _UNIT_STATE
+
+
+def _worker_init() -> None:
     from threadpoolctl import threadpool_limits
-    from oracle import qsa_oracle as O
+    _UNIT_STATE["_limits"] = threadpool_limits(limits=1)   # one BLAS thread per worker
 
-    done = 0
-    scale = 1.0 / 16.0
-    with threadpool_limits(limits=1):
-        if wl.kind == "prefill":
+
+def oracle_unit(task) -> int:
+    """One unit of oracle work: task = (scratch dir, kind, unit index, meta)."""
+    from oracle import qsa_oracle as O
+    path, kind, u, meta = task
+    A = _unit_arrays(path)
+    ps, scale = meta["page_size"], 1.0 / 16.0
+    scales = meta.get("kv_scales")
+    if kind == "indexshare":
+        b, j = divmod(u, meta["reuse_steps"])
+        j += 1
+        cap = np.asarray(A["cap_pos"][b, :int(A["cap_cnt"][b])])
+        O.indexshare_step(cap, int(A["q_pos"][b]), j, A["reuse_q"][j - 1, b], A["page_table"][b],
+                          A["k_pool"], A["v_pool"], ps, scale, kv_scales=scales)
+        return 1
+    t = u
+    b = int(A["q_req"][t])
+    p = int(A["q_pos"][t])
+    keys = A["comp"][int(A["comp_off"][b]):int(A["comp_off"][b + 1])]
+    if kind == "decode" and (p + 1) % 4 == 0:
+        # the query's own token completes block p // 4: its key joins the prefix keys
+        c = p // 4
+        keys = np.concatenate([keys, O.compress_blocks(np.asarray(A["last_block"][b])[None],
+                                                       np.array([4 * c]), meta["theta"])])
+    O.query(keys, A["idx_q"][t], A["idx_w"][t], A["q"][t], p, A["page_table"][b], A["k_pool"],
+            A["v_pool"], ps, scale, kv_scales=scales)
+    return 1
+
+
+class OracleBaseline:
+    """The oracle timed on the host beside the GPU result: once on one thread, once
+    over `workers` spawned processes.  The pool is started before anything touches
+    the GPU, so its processes never inherit a GPU context."""
+
+    def __init__(self, workers: int):
+        import multiprocessing as mp
+        self.workers = workers
+        self.pool = mp.get_context("spawn").Pool(workers, initializer=_worker_init) if workers > 1 else None
+
+    def close(self) -> None:
+        if self.pool is not None:
+            self.pool.terminate()
+            self.pool.join()
+
+    def _stage(self, wl, kv: str):
+        """Write the units' inputs to a scratch directory; returns (dir, kind, units,
+        meta, timed setup seconds).  Prefix keys are built untimed; a prefill chunk's
+        own compressed keys are built inside the timed region, as the GPU step does."""
+        import tempfile
+        from oracle import qsa_oracle as O
+        root = "/dev/shm" if os.path.isdir("/dev/shm") else None
+        path = tempfile.mkdtemp(prefix="qsa_oracle_", dir=root)
+        k_pool, v_pool, scales = O.kv_pools(wl, kv)
+        meta = {"page_size": wl.page_size, "theta": wl.rope_theta, "kv_scales": scales,
+                "reuse_steps": wl.reuse_steps}
+        arrays = {"k_pool": k_pool, "v_pool": v_pool, "page_table": wl.page_table, "q_req": wl.q_req,
+                  "q_pos": wl.q_pos, "idx_q": wl.idx_q, "idx_w": wl.idx_w, "q": wl.q}
+        timed = 0.0
+        kind = wl.kind
+        if kind == "prefill":
             pre = [O.build_index_state(wl.raw_idx_k[b], int(wl.prefix_len[b]), wl.rope_theta)[0]
                    for b in range(wl.batch)]
             t0 = time.perf_counter()
@@ -246,53 +328,75 @@ def cpu_baseline(wl, seconds: float, kv: str = "bf16") -> dict:
                 blk = O.compress_blocks(wl.raw_idx_k[b][4 * c0:4 * c1].reshape(-1, 4, 128),
                                         4 * np.arange(c0, c1), wl.rope_theta)
                 comp.append(np.concatenate([pre[b], blk]))
-            for t in range(wl.total_q):
-                b = int(wl.q_req[t])
-                O.query(comp[b], wl.idx_q[t], wl.idx_w[t], wl.q[t], int(wl.q_pos[t]), wl.page_table[b],
-                        wl.k_pool, wl.v_pool, wl.page_size, scale)
-                done += 1
-                if time.perf_counter() - t0 >= seconds:
-                    break
-            el = time.perf_counter() - t0
-            return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                    "sample": f"the chunk's compressed keys, then the first {done} of its "
-                              f"{wl.total_q} query rows, float64 numpy oracle, {el:.1f} s"}
-        prefix = [O.build_index_state(wl.raw_idx_k[b], int(wl.q_pos[b]), wl.rope_theta)[0]
-                  for b in range(wl.batch)]
-        if wl.kind == "indexshare":
-            cap = {}
+            timed = time.perf_counter() - t0
+            units = list(range(wl.total_q))
+        else:
+            # keys of the blocks complete before each query's own token
+            comp = [O.build_index_state(wl.raw_idx_k[b], int(wl.q_pos[b]), wl.rope_theta)[0]
+                    for b in range(wl.batch)]
+            last = np.zeros((wl.batch, 4, 128), np.uint16)
             for b in range(wl.batch):
                 p = int(wl.q_pos[b])
-                cap[b] = O.query(_oracle_keys_at(O, wl, b, prefix[b], p), wl.idx_q[b], wl.idx_w[b],
-                                 wl.q[b], p, wl.page_table[b], wl.k_pool, wl.v_pool, wl.page_size,
-                                 scale)["positions"]
-            t0 = time.perf_counter()
-            while True:
+                c = p // 4
+                last[b, :p + 1 - 4 * c] = wl.raw_idx_k[b][4 * c:p + 1]
+            arrays["last_block"] = last
+            units = list(range(wl.batch))
+            if kind == "indexshare":
+                cap_pos = np.full((wl.batch, O.MAX_SELECTED), -1, np.int64)
+                cap_cnt = np.zeros(wl.batch, np.int64)
+                with_block = [comp[b] if (int(wl.q_pos[b]) + 1) % 4 else np.concatenate(
+                    [comp[b], O.compress_blocks(last[b][None], np.array([4 * (int(wl.q_pos[b]) // 4)]),
+                                                wl.rope_theta)]) for b in range(wl.batch)]
                 for b in range(wl.batch):
-                    j = 1 + done % wl.reuse_steps
-                    O.indexshare_step(cap[b], int(wl.q_pos[b]), j, wl.reuse_q[j - 1, b], wl.page_table[b],
-                                      wl.k_pool, wl.v_pool, wl.page_size, scale)
-                    done += 1
-                el = time.perf_counter() - t0
-                if el >= seconds:
-                    break
-            return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                    "sample": f"{done} IndexShare reuse steps (request x step) of the same workload, "
-                              f"float64 numpy oracle, {el:.1f} s"}
-        k_pool, v_pool, scales = O.kv_pools(wl, kv)
-        t0 = time.perf_counter()
-        while True:
-            for b in range(wl.batch):
-                p = int(wl.q_pos[b])
-                O.query(_oracle_keys_at(O, wl, b, prefix[b], p), wl.idx_q[b], wl.idx_w[b], wl.q[b], p,
-                        wl.page_table[b], k_pool, v_pool, wl.page_size, scale, kv_scales=scales)
-                done += 1
-            el = time.perf_counter() - t0
-            if el >= seconds:
-                break
-    return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} decode queries ({done // wl.batch} passes over the batch of "
-                      f"{wl.batch}) of the same workload, float64 numpy oracle, {el:.1f} s"}
+                    pos = O.query(with_block[b], wl.idx_q[b], wl.idx_w[b], wl.q[b], int(wl.q_pos[b]),
+                                  wl.page_table[b], k_pool, v_pool, wl.page_size, 1.0 / 16.0,
+                                  kv_scales=scales)["positions"]
+                    cap_pos[b, :len(pos)] = pos
+                    cap_cnt[b] = len(pos)
+                arrays.update(cap_pos=cap_pos, cap_cnt=cap_cnt, reuse_q=wl.reuse_q)
+                units = list(range(wl.batch * wl.reuse_steps))
+        arrays["comp"] = np.concatenate(comp)
+        arrays["comp_off"] = np.concatenate([[0], np.cumsum([len(c) for c in comp])]).astype(np.int64)
+        for name, arr in arrays.items():
+            np.save(os.path.join(path, name + ".npy"), np.ascontiguousarray(arr))
+        return path, kind, units, meta, timed
+
+    def run(self, wl, seconds: float, seconds_single: float, kv: str = "bf16") -> dict:
+        import shutil
+        from threadpoolctl import threadpool_limits
+        path, kind, units, meta, t_setup = self._stage(wl, kv)
+        what = {"decode": "decode queries", "prefill": "prefill query rows",
+                "indexshare": "IndexShare reuse steps (request x step)"}[kind]
+        try:
+            tasks = [(path, kind, u, meta) for u in units]
+            # one thread: whole passes over the units, for about seconds_single
+            with threadpool_limits(limits=1):
+                oracle_unit(tasks[0])               # maps the inputs, untimed
+                done, t0 = 0, time.perf_counter()
+                while time.perf_counter() - t0 < seconds_single:
+                    for task in tasks:
+                        done += oracle_unit(task)
+                        if kind == "prefill" and time.perf_counter() - t0 >= seconds_single:
+                            break
+                el1 = time.perf_counter() - t0 + t_setup
+            single = {"value": done / el1, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                      "sample": f"{done} {what} of the same workload on one thread, float64 numpy "
+                                f"oracle, {el1:.1f} s"}
+            if self.pool is None:
+                return dict(single, single_thread=dict(single))
+            # every worker: the same units, cycled through the pool, for about `seconds`
+            self.pool.map(oracle_unit, tasks[:self.workers] * 1, chunksize=1)   # warm, untimed
+            done, t0 = 0, time.perf_counter()
+            rounds = max(1, (4 * self.workers + len(tasks) - 1) // len(tasks))
+            while time.perf_counter() - t0 < seconds:
+                done += sum(self.pool.imap_unordered(oracle_unit, tasks * rounds, chunksize=1))
+            el = time.perf_counter() - t0 + t_setup
+            return {"value": done / el, "unit": "tokens/s", "cores": self.workers, "kind": "oracle",
+                    "sample": f"{done} {what} of the same workload over {self.workers} worker "
+                              f"processes (one BLAS thread each), float64 numpy oracle, {el:.1f} s",
+                    "single_thread": single}
+        finally:
+            shutil.rmtree(path, ignore_errors=True)
 
 
 # ------------------------------------------------------------------ GPU timing
@@ -427,11 +531,23 @@ def projection_overlap(torch, sets, hidden: int, timed, ref_out) -> dict:
                    "replays, outputs checked against the eager step"}
 
 
-def time_stages(torch, sets, stages, K: int) -> dict:
-    """Mean duration (us) of each stage from HIP events recorded on the launch
-    stream; the launches queue behind a spin kernel so the GPU runs them back to
-    back."""
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(K)]
+def time_stages(torch, sets, stages, K: int):
+    """Mean durations (us) of each stage and of each kernel from HIP events, over K
+    back-to-back steps queued on the launch stream behind a spin kernel.
+
+    stages: (name, fn(d), kernels) with the kernel names the stage's call launches in
+    order.  Events recorded on the stream before the step and after every call time
+    the stages.  Each kernel gets a (start, stop) event pair that the library passes to
+    its launch (qsa_profile_kernel_events, hipExtLaunchKernelGGL), so a kernel's time
+    is its own dispatch's duration.  Returns ({stage or kernel: mean us}, {stage:
+    [p10, p50, p90]}); a kernel launched several times in a step is summed per step."""
+    from block_sparse_attention_c4_amd import binding as Bnd
+    n_k = sum(len(k) for _, _, k in stages)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(1 + len(stages) + 2 * n_k)]
+          for _ in range(K)]
+    for row in ev:                     # torch creates an event at its first record
+        for e in row:
+            e.record()
     torch.cuda.synchronize()
     if hasattr(torch.cuda, "_sleep"):
         torch.cuda._sleep(int(100e6))
@@ -439,18 +555,32 @@ def time_stages(torch, sets, stages, K: int) -> dict:
         d = sets[i % len(sets)]
         e = ev[i]
         e[0].record()
-        for j, (_, fn) in enumerate(stages):
+        kp = 1 + len(stages)           # this step's kernel event pairs start here
+        for j, (_, fn, kernels) in enumerate(stages):
+            Bnd.qsa_profile_kernel_events(e[kp:kp + 2 * len(kernels)])
             fn(d)
-            e[j + 1].record()
+            e[1 + j].record()
+            kp += 2 * len(kernels)
     torch.cuda.synchronize()
-    st = {name: [] for name, _ in stages}
-    st["step"] = []
+    st = {"step": []}
+    for name, _, kernels in stages:
+        st[name] = []
+        for k in kernels:
+            st.setdefault(k, [])
     for e in ev:
-        for j, (name, _) in enumerate(stages):
-            st[name].append(e[j].elapsed_time(e[j + 1]))
-        st["step"].append(e[0].elapsed_time(e[-1]))
+        per_kernel = {}
+        kp = 1 + len(stages)
+        for j, (name, _, kernels) in enumerate(stages):
+            st[name].append(e[j].elapsed_time(e[1 + j]))
+            for k in kernels:
+                per_kernel[k] = per_kernel.get(k, 0.0) + e[kp].elapsed_time(e[kp + 1])
+                kp += 2
+        for k, v in per_kernel.items():
+            st[k].append(v)
+        st["step"].append(e[0].elapsed_time(e[len(stages)]))
+    stage_names = ["step"] + [name for name, _, _ in stages]
     return {k: float(np.mean(v)) * 1e3 for k, v in st.items()}, \
-        {k: [round(float(np.percentile(v, q)) * 1e3, 2) for q in (10, 50, 90)] for k, v in st.items()}
+        {k: [round(float(np.percentile(st[k], q)) * 1e3, 2) for q in (10, 50, 90)] for k in stage_names}
 
 
 def main() -> int:
@@ -461,7 +591,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--sets", type=int, default=None, help="input copies cycled through (cold cache)")
     ap.add_argument("--stage-steps", type=int, default=None)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="oracle time over the worker processes")
+    ap.add_argument("--cpu-seconds-single", type=float, default=6.0,
+                    help="oracle time on one thread, reported beside")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the plain-launch and warm step timings (profiled runs: every traced "
@@ -493,6 +626,16 @@ def main() -> int:
     nsets = args.sets if args.sets is not None else cfg["sets"]
     K = args.stage_steps if args.stage_steps is not None else min(200, steps)
 
+    # the oracle's worker processes start before anything touches the GPU
+    baseline = None if args.no_cpu_baseline else OracleBaseline(oracle_workers())
+    try:
+        return run(args, cfg, kind, steps, warmup, nsets, K, baseline)
+    finally:
+        if baseline is not None:
+            baseline.close()
+
+
+def run(args, cfg, kind, steps, warmup, nsets, K, baseline) -> int:
     import torch
     from block_sparse_attention_c4_amd import runner, synth
 
@@ -566,10 +709,13 @@ def main() -> int:
     ms_unfused = None
     if fused and not args.headline_only:
         ms_unfused, _ = timed([step_fn(d, False) for d in sets], [d.out for d in sets], [ref_out] * len(sets))
+    kernels = stage_kernels(kind, base, fused)
     if fused:
-        stages = [("build_index", lambda d: d.build_index()), ("attend", lambda d: d.attend())]
+        stages = [("build_index", lambda d: d.build_index(), kernels["build_index"]),
+                  ("attend", lambda d: d.attend(), kernels["attend"])]
     else:
-        stages = [("build", build_fn), ("index", lambda d: d.index()), ("attend", lambda d: d.attend())]
+        stages = [("build", build_fn, kernels["build"]), ("index", lambda d: d.index(), kernels["index"]),
+                  ("attend", lambda d: d.attend(), kernels["attend"])]
     stage_us, stage_pct = time_stages(torch, sets, stages, K)
 
     # ---------------- the indexer on a second stream beside a projection
@@ -602,9 +748,12 @@ def main() -> int:
             torch.cuda.synchronize()
             refs.append(d.out.clone())
         ms_reuse = timed(fns, [d.out for d in sets], refs)[0] / J
+        n_ws = runner.B.qsa_workspace_bytes(base.dims, runner.B.QSA_OP_GQA_DECODE, wl.batch, 0, 4)
+        reuse_kernels = ["attn_kernel"] + (["combine_kernel"] if n_ws > 0 else [])
         rst, _ = time_stages(torch, sets, [("reuse", lambda d: d.attend(
-            q=d.reuse_q[J - 1], extra=extras[J - 1], n_extra=4))], K)
-        reuse = {"ms": ms_reuse, "attend_us": rst["reuse"]}
+            q=d.reuse_q[J - 1], extra=extras[J - 1], n_extra=4), reuse_kernels)], K)
+        reuse = {"ms": ms_reuse, "attend_us": rst["reuse"], "kernels": reuse_kernels,
+                 "kernel_us": {k: rst[k] for k in reuse_kernels}}
 
     if args.calib_copy_mib:
         # one elementwise kernel that reads and writes exactly n bytes: the scale of
@@ -616,7 +765,6 @@ def main() -> int:
         torch.mul(a, 1.0, out=b)
         torch.cuda.synchronize()
 
-    kernels = stage_kernels(kind, kv, fused)
     config = {"workload": args.workload, "batch": wl.batch, "seed": wl.seed, "context": cfg["context"],
               "q_heads": 16, "kv_heads": 2, "head_dim": 256, "indexer": "4x128", "topk_blocks": 512,
               "page_size": wl.page_size, "input_sets": len(sets), "launch": launch}
@@ -631,8 +779,11 @@ def main() -> int:
     result = {"metric": cfg["metric"], "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": steps,
               "warmup": warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
               "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": config}
-    result["stage_us"] = {k: round(v, 2) for k, v in stage_us.items()}
+    stage_names = [name for name, _, _ in stages]
+    result["stage_us"] = {k: round(stage_us[k], 2) for k in ["step"] + stage_names}
     result["stage_us_p10_p50_p90"] = stage_pct
+    result["kernel_us"] = {k: round(v, 2) for k, v in stage_us.items() if k not in result["stage_us"]}
+    result["stage_kernels"] = {name: ks for name, _, ks in stages}
     if ms_stream is not None:
         result["ms_per_step_stream_launches"] = round(ms_stream, 5)
         result["ms_per_step_warm"] = round(ms_warm, 5)
@@ -642,10 +793,22 @@ def main() -> int:
         result["projection_overlap"] = overlap
     result["timing"] = (f"value and ms_per_step: {steps} steps after {warmup} warm-up steps, host clock "
                         f"around synchronize(), {len(sets)} input copies cycled ({launch}); "
-                        "stage_us: means of HIP events on the launch stream over back-to-back steps; "
+                        "stage_us: means of HIP events on the launch stream over "
+                        f"{K} back-to-back steps; kernel_us: means of each kernel's start/stop HIP "
+                        "events, set from its dispatch (qsa_profile_kernel_events); "
                         "ms_per_step_warm: one input copy, hipGraph replays; "
                         "ms_per_step_builder_separate: the same steps with the builder as its own call")
 
+    def hbm_roofline(kernel, entry, nbytes_kernel, us):
+        achieved = nbytes_kernel / (us * 1e-6) / 1e9
+        return {"bound": "hbm", "kernel": kernel, "entry_point": entry, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": load_traffic(args.workload, kernel), "bytes_per_launch": int(nbytes_kernel),
+                "kernel_us": round(us, 2),
+                "how": "algorithmic bytes of one launch over the kernel's mean duration from HIP events "
+                       "(kernel_us)"}
+
+    combined = "combine_kernel" in kernels["attend"]
     if kind == "prefill":
         work = prefill_work(wl, counts)
         config["chunk"] = int(wl.total_q)
@@ -656,12 +819,17 @@ def main() -> int:
         result["stage_tflops"] = {"index_scoring": round(score_tf, 1), "attend": round(attn_tf, 1)}
         result["algorithmic"] = {"score_flops": work["score_flops"], "attn_flops": work["attn_flops"],
                                  "unique_bytes": work["bytes"]}
-        # the scorer's FLOPs over the whole indexer call (scorer + code select): a
-        # lower bound on the scorer kernel's own rate
-        result["roofline"] = {"bound": "mfma", "kernel": kernels["index"], "entry_point": ENTRY["index"],
-                              "achieved": round(score_tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                              "unit": "TFLOP/s", "frac": round(score_tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                              "traffic": load_traffic(args.workload, "index")}
+        us = stage_us["score_mfma_kernel"]
+        tf = work["score_flops"] / (us * 1e-6) / 1e12
+        result["roofline"] = {"bound": "mfma", "kernel": "score_mfma_kernel", "entry_point": ENTRY["index"],
+                              "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                              "traffic": load_traffic(args.workload, "score_mfma_kernel"),
+                              "flops_per_launch": work["score_flops"], "kernel_us": round(us, 2),
+                              "how": "the scorer's FLOPs (4 heads x 128 dims x 2 per visible block of "
+                                     "every query) over its mean duration from HIP events; "
+                                     "stage_tflops.index_scoring is the same FLOPs over the whole "
+                                     "indexer call"}
     elif kind == "indexshare":
         nbytes = decode_bytes(wl, counts)
         att = decode_bytes(wl, counts, n_extra=wl.reuse_steps)["attend"]
@@ -670,15 +838,14 @@ def main() -> int:
         result["ms_per_step_without_reuse"] = round(ms_step, 5)
         result["tokens_per_s_without_reuse"] = round(wl.batch / (ms_step * 1e-3), 1)
         result["reuse_attend_us"] = round(reuse["attend_us"], 2)
+        result["reuse_kernel_us"] = {k: round(v, 2) for k, v in reuse["kernel_us"].items()}
         result["reuse_timing"] = (f"MTP iterations of {wl.reuse_steps} reuse steps, one per input copy, "
                                   f"in one hipGraph per round; time divided by {wl.reuse_steps}")
         result["algorithmic_bytes"] = nbytes
         result["algorithmic_bytes_reuse_step"] = att
-        achieved = att / (reuse["attend_us"] * 1e-6) / 1e9
-        result["roofline"] = {"bound": "hbm", "kernel": kernels["attend"], "entry_point": ENTRY["attend"],
-                              "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                              "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                              "traffic": load_traffic(args.workload, "attend")}
+        split = attend_kernel_bytes(att, wl.batch, "combine_kernel" in reuse["kernels"])
+        result["roofline"] = hbm_roofline("attn_kernel", ENTRY["attend"], split["attn_kernel"],
+                                          reuse["kernel_us"]["attn_kernel"])
     elif kind == "verify":
         nbytes = verify_bytes(wl, base.sel_pos.cpu().numpy(), counts)
         config["query_tokens_per_request"] = int(wl.total_q // wl.batch)
@@ -688,13 +855,9 @@ def main() -> int:
         result["step_hbm_gbps"] = round(nbytes["step"] / (ms_step * 1e-3) / 1e9, 1)
         result["step_hbm_frac"] = round(nbytes["step"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
         result["algorithmic_bytes"] = nbytes
-        dom = "attend"   # it holds the step's longest kernel (attn_kernel) and most of its bytes
-        achieved = nbytes[dom] / (stage_us[dom] * 1e-6) / 1e9
-        entry = "qsa_sparse_gqa_prefill" if dom == "attend" else ENTRY[dom]
-        result["roofline"] = {"bound": "hbm", "kernel": kernels[dom], "entry_point": entry,
-                              "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                              "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                              "traffic": load_traffic(args.workload, dom)}
+        split = attend_kernel_bytes(nbytes["attend"], wl.total_q, combined)
+        result["roofline"] = hbm_roofline("attn_kernel", "qsa_sparse_gqa_prefill", split["attn_kernel"],
+                                          stage_us["attn_kernel"])
     else:
         nbytes = decode_bytes(wl, counts, kv_bytes=1 if kv == "fp8" else 2)
         result["value"] = round(wl.batch / (ms_step * 1e-3), 1)
@@ -702,18 +865,17 @@ def main() -> int:
         result["step_hbm_gbps"] = round(nbytes["step"] / (ms_step * 1e-3) / 1e9, 1)
         result["step_hbm_frac"] = round(nbytes["step"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
         result["algorithmic_bytes"] = nbytes
-        dom = "attend"   # it holds the step's longest kernel (attn_kernel) and most of its bytes
-        achieved = nbytes[dom] / (stage_us[dom] * 1e-6) / 1e9
-        entry = "qsa_sparse_gqa_decode_fp8" if (dom == "attend" and kv == "fp8") else ENTRY[dom]
-        result["roofline"] = {"bound": "hbm", "kernel": kernels[dom], "entry_point": entry,
-                              "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                              "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                              "traffic": load_traffic(args.workload, dom)}
+        split = attend_kernel_bytes(nbytes["attend"], wl.batch, combined)
+        entry = "qsa_sparse_gqa_decode_fp8" if kv == "fp8" else ENTRY["attend"]
+        result["roofline"] = hbm_roofline("attn_kernel", entry, split["attn_kernel"], stage_us["attn_kernel"])
 
     if not args.no_ceilings:
         result["measured_ceilings"] = measured_ceilings(torch)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, kv)
+        if "step_hbm_gbps" in result:
+            result["step_frac_of_measured_copy"] = round(
+                result["step_hbm_gbps"] / result["measured_ceilings"]["stream_copy_gbps"], 4)
+    if baseline is not None:
+        result["cpu_baseline"] = baseline.run(wl, args.cpu_seconds, args.cpu_seconds_single, kv)
         result["cpu_baseline"]["host"] = host_cpu()
     print(json.dumps(result), flush=True)
     return 0

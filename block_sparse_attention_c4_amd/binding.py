@@ -144,8 +144,10 @@ def _check(status: int, where: str) -> None:
 
 
 def qsa_profile_kernel_events(events) -> None:
-    """events: torch.cuda.Event objects (or raw hipEvent_t handles) that the calling
-    thread's next QSA call records after its first len(events) kernels."""
+    """events: torch.cuda.Event objects (or raw hipEvent_t handles), a (start, stop)
+    pair for each of the first len(events) / 2 kernels of the calling thread's next
+    QSA call; the events must have been created (torch creates one at its first
+    record)."""
     handles = [e.cuda_event if hasattr(e, "cuda_event") else int(e) for e in events]
     arr = (ctypes.c_void_p * max(len(handles), 1))(*handles)
     _check(lib().qsa_profile_kernel_events(arr, len(handles)), "qsa_profile_kernel_events")

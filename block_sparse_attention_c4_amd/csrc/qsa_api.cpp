@@ -28,10 +28,10 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int hip_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_E_HIP; }
 
-// HIP events that the calling thread asked the next call to record after its
-// kernels (qsa_profile_kernel_events).  A call's CallScope drops the request when
-// the call returns, whether or not every event was recorded.
-constexpr int kMaxProfileEvents = 8;
+// (start, stop) HIP event pairs that the calling thread asked the next call to set
+// for its kernels (qsa_profile_kernel_events).  A call's CallScope drops the request
+// when the call returns, whether or not every pair was used.
+constexpr int kMaxProfileEvents = 16;
 struct ProfileEvents {
   hipEvent_t ev[kMaxProfileEvents];
   int n = 0, next = 0;
@@ -45,8 +45,14 @@ struct CallScope {
 }  // namespace
 
 namespace qsa {
-void note_launch(hipStream_t stream) {
-  if (t_profile.next < t_profile.n) hipEventRecord(t_profile.ev[t_profile.next++], stream);
+void launch_events(hipEvent_t* start, hipEvent_t* stop) {
+  if (t_profile.next + 1 < t_profile.n) {
+    *start = t_profile.ev[t_profile.next];
+    *stop = t_profile.ev[t_profile.next + 1];
+    t_profile.next += 2;
+  } else {
+    *start = *stop = nullptr;
+  }
 }
 }  // namespace qsa
 
@@ -67,7 +73,7 @@ const char* qsa_status_string(int status) {
 }
 
 int qsa_profile_kernel_events(void* const* events, int32_t n_events) {
-  if (n_events < 0 || n_events > kMaxProfileEvents) return QSA_E_SHAPE;
+  if (n_events < 0 || n_events > kMaxProfileEvents || n_events % 2 != 0) return QSA_E_SHAPE;
   if (n_events > 0 && !events) return QSA_E_NULL;
   for (int i = 0; i < n_events; ++i) {
     if (!events[i]) return QSA_E_NULL;

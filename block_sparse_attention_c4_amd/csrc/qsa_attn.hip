@@ -539,15 +539,13 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   const bool one_step = a.splits > 1 || nblk <= 256;
   auto kern = a.fp8 ? (one_step ? attn_kernel<true, 1> : attn_kernel<true, 2>)
                     : (one_step ? attn_kernel<false, 1> : attn_kernel<false, 2>);
-  hipLaunchKernelGGL(kern, dim3(nblk), dim3(kThreads), 0, stream, a.q, a.q_req, a.k_pool,
+  QSA_LAUNCH(kern, dim3(nblk), dim3(kThreads), 0, stream, a.q, a.q_req, a.k_pool,
                      a.v_pool, a.page_table, a.pt_stride, a.page_size, a.sel_pos, a.sel_count,
                      a.sel_stride, a.extra_pos, a.n_extra, scale_log2, v_scale, a.splits, a.part,
                      a.out, a.lse);
-  note_launch(stream);
   if (a.splits > 1) {
-    hipLaunchKernelGGL(combine_kernel, dim3(a.total_q * kKVHeads), dim3(256), 0, stream, a.part,
+    QSA_LAUNCH(combine_kernel, dim3(a.total_q * kKVHeads), dim3(256), 0, stream, a.part,
                        a.splits, v_scale, a.out, a.lse);
-    note_launch(stream);
   }
   return hipGetLastError();
 }

@@ -113,10 +113,9 @@ hipError_t launch_build(const BuildArgs& a, hipStream_t stream) {
   // blocks touched by n new tokens starting anywhere: at most n/4 + 2
   const int units = a.max_new / kBlock + 2;
   dim3 grid((units + kUnits - 1) / kUnits, a.batch);
-  hipLaunchKernelGGL(build_kernel, grid, dim3(64), 0, stream, a.new_k, a.cu_new, a.len_before,
+  QSA_LAUNCH(build_kernel, grid, dim3(64), 0, stream, a.new_k, a.cu_new, a.len_before,
                      a.page_table, a.pt_stride, a.page_size, a.ring, a.comp, a.new_mpos,
                      a.ring_mpos, rope);
-  note_launch(stream);
   return hipGetLastError();
 }
 

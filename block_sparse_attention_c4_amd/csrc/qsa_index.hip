@@ -285,8 +285,8 @@ __device__ __forceinline__ void score_body(
   }
 
   // write the range's scores and each group's maximum: lane l covers group l / 4,
-  // blocks 4 (l % 4) .. +3.  Past the last block the scores repeat the last block's
-  // (the loads were clamped), so the maximum is that of the visible blocks.
+  // blocks 4 (l % 4) .. +3.  Past the last block the computed scores repeat the last
+  // block's (the loads were clamped), so the maximum is that of the visible blocks.
   const int gstride = score_stride / kScoreGroup;
   for (int i0 = 0; i0 < ng; i0 += 16) {
     const int i = min(i0 + (lane >> 2), ng - 1);
@@ -299,15 +299,13 @@ __device__ __forceinline__ void score_body(
     m = fmaxf(m, dpp_f<0x4e>(m));            // quad_perm [2,3,0,1]
     if (i0 + (lane >> 2) < ng) {
       if ((lane & 3) == 0) gmax[(size_t)t * gstride + (tg & 0xffff)] = m;
+      // the group's whole 16 scores, -inf past the last block (the select reads
+      // groups whole)
       const int c = (tg & 0xffff) * kScoreGroup + 4 * (lane & 3);
-      float* dst = scores + (size_t)t * score_stride + c;
-      if (c + 3 < n_c) {
-        *reinterpret_cast<f32x4_t*>(dst) = v;
-      } else {
+      f32x4_t o = v;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (c + k < n_c) dst[k] = v[k];
-      }
+      for (int k = 0; k < 4; ++k) o[k] = c + k < n_c ? v[k] : -INFINITY;
+      *reinterpret_cast<f32x4_t*>(scores + (size_t)t * score_stride + c) = o;
     }
   }
 }
@@ -485,7 +483,9 @@ score_multi_kernel(int nq, const uint16_t* __restrict__ idx_q, const float* __re
     const int c = u.g * kScoreGroup + (lane & 15);
     const bool ok = c < r.nc;
     const float m = row16_max(ok ? s : -INFINITY);
-    if (ok) scores[(size_t)r.t * score_stride + c] = s;
+    // the query's groups whole, -inf past its last block (the select reads groups whole)
+    if (c < ((r.nc + kScoreGroup - 1) & ~(kScoreGroup - 1)))
+      scores[(size_t)r.t * score_stride + c] = ok ? s : -INFINITY;
     if ((lane & 15) == 0 && u.g * kScoreGroup < r.nc) gmax[(size_t)r.t * gstride + u.g] = m;
   };
 
@@ -573,13 +573,12 @@ hipError_t launch_index(const IndexArgs& a, hipStream_t stream) {
       // passes: one per window, plus one per request boundary inside a window
       const int64_t passes = std::min<int64_t>(nq, (nq + kWin - 1) / kWin + a.batch - 1);
       const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(passes * gpq / 2, 4096));
-      hipLaunchKernelGGL(score_multi_kernel, dim3(grid), dim3(64), 0, stream, nq,
+      QSA_LAUNCH(score_multi_kernel, dim3(grid), dim3(64), 0, stream, nq,
                          a.idx_q + (size_t)q0 * kIdxHeads * kIdxDim,
                          a.idx_w + (size_t)q0 * kIdxHeads, a.q_req + q0, a.q_pos + q0,
                          a.page_table, a.pt_stride, a.page_size, a.comp,
                          a.scores + (size_t)q0 * a.score_stride, a.score_stride,
                          a.gmax_f + (size_t)q0 * (a.score_stride / kScoreGroup));
-      note_launch(stream);
     }
     launch_topk(a, stream);
     return hipGetLastError();
@@ -596,12 +595,11 @@ hipError_t launch_index(const IndexArgs& a, hipStream_t stream) {
     const int64_t want = std::min<int64_t>(groups_bound, 4096);
     const int grid = (int)std::max<int64_t>(
         1, std::max<int64_t>(want, (groups_bound + kWaveGroups - 1) / kWaveGroups));
-    hipLaunchKernelGGL(score_kernel, dim3(grid), dim3(64), 0, stream, nq,
+    QSA_LAUNCH(score_kernel, dim3(grid), dim3(64), 0, stream, nq,
                        a.idx_q + (size_t)q0 * kIdxHeads * kIdxDim, a.idx_w + (size_t)q0 * kIdxHeads,
                        a.q_req + q0, a.q_pos + q0, a.page_table, a.pt_stride, a.page_size, a.comp,
                        a.scores + (size_t)q0 * a.score_stride, a.score_stride,
                        a.gmax_f + (size_t)q0 * (a.score_stride / kScoreGroup));
-    note_launch(stream);
   }
   launch_topk(a, stream);
   return hipGetLastError();
@@ -631,12 +629,11 @@ hipError_t launch_index_ingest(const IndexArgs& a, const IngestArgs& f, hipStrea
     ing.new_mpos = f.new_mpos ? f.new_mpos + (size_t)q0 * 3 : nullptr;
     ing.req0 = q0;
     // nq work groups of the queries' own, then the scorer's
-    hipLaunchKernelGGL(score_build_kernel, dim3(nq + grid), dim3(64), 0, stream, nq,
+    QSA_LAUNCH(score_build_kernel, dim3(nq + grid), dim3(64), 0, stream, nq,
                        a.idx_q + (size_t)q0 * kIdxHeads * kIdxDim, a.idx_w + (size_t)q0 * kIdxHeads,
                        a.q_pos + q0, a.page_table, a.pt_stride, a.page_size, a.comp,
                        a.scores + (size_t)q0 * a.score_stride, a.score_stride,
                        a.gmax_f + (size_t)q0 * (a.score_stride / kScoreGroup), ing);
-    note_launch(stream);
   }
   launch_topk(a, stream);
   return hipGetLastError();

@@ -1,15 +1,30 @@
 // Internal launch interface between the C ABI (qsa_api.cpp) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
+// Every kernel launch of the library.  When the calling thread asked for kernel
+// timing, the launch takes the next (start, stop) event pair, which the runtime sets
+// from the dispatch's own start and end timestamps.
+#define QSA_LAUNCH(kernel, grid, block, shmem, stream, ...)                                  \
+  do {                                                                                       \
+    hipEvent_t qsa_ev0_ = nullptr, qsa_ev1_ = nullptr;                                       \
+    ::qsa::launch_events(&qsa_ev0_, &qsa_ev1_);                                              \
+    if (qsa_ev0_ != nullptr)                                                                 \
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, qsa_ev0_, qsa_ev1_, 0u,      \
+                            __VA_ARGS__);                                                    \
+    else                                                                                     \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                   \
+  } while (0)
+
 namespace qsa {
 
-// Called after every kernel launch: records the next of the HIP events that the
-// calling thread asked for with qsa_profile_kernel_events, if any are left.
-void note_launch(hipStream_t stream);
+// Start and stop events for the next kernel launch, when the calling thread asked for
+// kernel timing (qsa_profile_kernel_events) and pairs are left; both null otherwise.
+void launch_events(hipEvent_t* start, hipEvent_t* stop);
 
 struct RopeTable {
   double inv_freq[64];   // theta^(-2i/128), i < 64

@@ -687,19 +687,16 @@ rescore_kernel(const int* __restrict__ queue, const int32_t* __restrict__ q_req,
 hipError_t launch_index_mfma(const IndexArgs& a, hipStream_t stream) {
   const int n_ranges = (a.max_pos / kBlock + kPfRange - 1) / kPfRange;
   const int n_tiles = (a.total_q + kPfQ - 1) / kPfQ;
-  hipLaunchKernelGGL(score_mfma_kernel, dim3(n_ranges * n_tiles), dim3(kST), 0, stream, a.total_q,
+  QSA_LAUNCH(score_mfma_kernel, dim3(n_ranges * n_tiles), dim3(kST), 0, stream, a.total_q,
                      a.idx_q, a.idx_w, a.q_req, a.q_pos, a.page_table, a.pt_stride, a.page_size,
                      a.comp, a.codes, a.gmax, a.score_stride, n_ranges, n_tiles, a.queue);
-  note_launch(stream);
-  hipLaunchKernelGGL(topk_codes_kernel, dim3(a.total_q), dim3(kTT), 0, stream, a.codes, a.gmax,
+  QSA_LAUNCH(topk_codes_kernel, dim3(a.total_q), dim3(kTT), 0, stream, a.codes, a.gmax,
                      a.score_stride, a.q_req, a.q_pos, a.idx_q, a.idx_w, a.page_table, a.pt_stride,
                      a.page_size, a.comp, a.sel_blocks, a.sel_pos, a.sel_stride, a.sel_count, a.queue);
-  note_launch(stream);
   const int g = std::min(a.total_q, 256);
-  hipLaunchKernelGGL(rescore_kernel, dim3(g), dim3(256), 0, stream, a.queue, a.q_req, a.q_pos,
+  QSA_LAUNCH(rescore_kernel, dim3(g), dim3(256), 0, stream, a.queue, a.q_req, a.q_pos,
                      a.idx_q, a.idx_w, a.page_table, a.pt_stride, a.page_size, a.comp, a.scores,
                      a.score_stride);
-  note_launch(stream);
   launch_topk_queued(a, stream);
   return hipGetLastError();
 }

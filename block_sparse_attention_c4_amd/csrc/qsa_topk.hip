@@ -532,11 +532,551 @@ __device__ __forceinline__ void topk_row(int t, const float* __restrict__ scores
   if (tid == 0) sel_count[t] = base + pend;
 }
 
-__global__ void __launch_bounds__(kT)
-topk_kernel(const float* __restrict__ scores, int score_stride, const float* __restrict__ gmax,
+// ------------------------------------------------------------------ latency-bound select
+
+// The select of topk_kernel: one work group of kFT threads per row.  A row's time is
+// a chain of dependent steps, each a few hundred instructions per wave plus a
+// barrier; every instruction of a wave costs the SIMD it shares with the other waves,
+// so the group is kept to kFT = 256 threads (one wave per SIMD), and the work on the
+// row's scores is done four scores at a time.
+//   - The row's position and its 16-block group maxima (written by the scorer) are
+//     requested together at kernel start, the maxima before the row's length is known
+//     (the workspace row of maxima is score_stride / 16 long), so the first memory
+//     round trip brings both.  Thread i holds groups kGPT i .. kGPT i + kGPT - 1.
+//   - Lower bound t0: the 512th largest group maximum, from one linear-bin histogram
+//     pass (256 bins between the smallest and largest maximum), rounded down by one
+//     bin.  At least 512 groups reach it, hence at least 512 scores.
+//   - The candidate groups (maximum >= t0, about 520-600) are gathered in LDS, and
+//     each thread loads the scores of up to kCGT of them (the second and last round
+//     trip; the scorer writes a row's last group whole, -inf past the row's end).
+//   - Every float4 of those scores that holds a score >= t0 goes to an LDS list as it
+//     is (about 650 per row), with the index of its first block.
+//   - The exact 512th largest key T and how many keys equal to T are kept come from
+//     radix passes of 8 bits over key - t0 by the whole group, one barrier each (the
+//     list's keys >= t0 lie between t0 and the row's largest maximum).
+//   - The kept blocks (keys above T) and the blocks whose key equals T are marked in
+//     two LDS bitmaps.  One block scan of the words' (greater, equal) counts gives
+//     each word the kept blocks before it, and each kept block is written to its slot
+//     by the thread that holds its key (so the stores are spread over all threads),
+//     the need_eq lowest-indexed equal blocks included.
+// Rows of fewer than 1024 groups load their whole score row instead and take the
+// bound from 4-block quad maxima (or keep every score when the row has fewer than
+// 512 quads): with so few groups the 512th group maximum keeps most groups, and their
+// float4s above it can overflow the list.  Rows with too many candidates (heavy ties,
+// such as a row of equal scores) take an exact select over the row in memory.
+constexpr int kFT = 256;                          // threads per row
+constexpr int kFW = kFT / 64;
+constexpr int kGPT = kMaxBlocks / kScoreGroup / kFT;   // group maxima per thread: 16
+constexpr int kFCG = 1024;                        // candidate groups
+constexpr int kCGT = kFCG / kFT;                  // candidate groups per thread: 4
+constexpr int kShort = 2 * kTopK * kScoreGroup;   // rows below this many blocks are short
+constexpr int kSPT = kShort / kFT;                // short-row scores per thread: 64
+constexpr int kF4 = 1024;                         // listed float4s
+constexpr int kF4T = kF4 / kFT;                   // listed float4s per thread: 4
+constexpr int kBWords = kMaxBlocks / 32;          // bitmap words: 2048
+constexpr int kBWT = kBWords / kFT;               // bitmap words per thread: 8
+static_assert(kGPT % 4 == 0 && kSPT % 4 == 0 && kBWT % 4 == 0, "whole 16-byte accesses");
+static_assert(kFT >= 256, "one histogram bin per thread");
+static_assert(4 * kF4 < 65536, "bitmap counts packed in 16 bits");
+
+struct __attribute__((aligned(16))) SmemF {
+  f32x4_t lv[kF4];                   // listed float4s of scores
+  int lc[kF4];                       // the block of each one's first score
+  uint32_t gtb[kBWords];             // blocks with key > T
+  uint32_t eqb[kBWords];             // blocks with key == T
+  uint32_t pre[kBWords];             // per bitmap word: (equal before it) << 16 | (above before it)
+  uint32_t hist[256];                // lower-bound histogram
+  uint32_t rhist[3][256];            // the select's radix histograms (one per pass, cycled)
+  uint16_t cg[kFCG];                 // candidate groups
+  uint32_t red[2 * kFW];             // per-wave max / min
+  uint32_t wsum[kFW];                // block-scan wave totals
+  int misc[4];                       // [0] candidate groups, [1] listed float4s, [2] a published key
+};
+
+__shared__ SmemF sf;
+
+// Exclusive block-wide scan of one value per thread; .x = prefix, .y = total.
+__device__ __forceinline__ uint2 fscan(uint32_t v) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint32_t inc = (uint32_t)wave_inclusive_sum((int)v);
+  if (lane == 63) sf.wsum[w] = inc;
+  __syncthreads();
+  uint32_t before = 0u, total = 0u;
+#pragma unroll
+  for (int i = 0; i < kFW; ++i) {
+    const uint32_t x = sf.wsum[i];
+    before += i < w ? x : 0u;
+    total += x;
+  }
+  return make_uint2(before + inc - v, total);
+}
+
+// Slot base of this lane's `cnt` items in a shared counter (one LDS atomic per wave).
+__device__ __forceinline__ int wave_slots(int cnt, int* counter) {
+  const int lane = threadIdx.x & 63;
+  const int incl = wave_inclusive_sum(cnt);
+  const int wtot = __builtin_amdgcn_readlane(incl, 63);
+  int base = 0;
+  if (lane == 63 && wtot > 0) base = atomicAdd(counter, wtot);
+  return __builtin_amdgcn_readlane(base, 63) + incl - cnt;
+}
+
+// Block-wide max and min of one key per thread (min over non-zero keys); one barrier.
+__device__ __forceinline__ uint2 block_max_min(uint32_t mx, uint32_t mn) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  mx = wave_max_u32(mx);
+  mn = wave_min_u32(mn);
+  if (lane == 0) {
+    sf.red[w] = mx;
+    sf.red[kFW + w] = mn;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kFW; ++i) {
+    mx = max(mx, sf.red[i]);
+    mn = min(mn, sf.red[kFW + i]);
+  }
+  return make_uint2(mx, mn);
+}
+
+// The bin of a 256-bin histogram that holds the kk-th largest entry, found by every
+// wave at once (lane l reads bins 4l..4l+3): .x = bin, .y = rank of the entry inside
+// the bin (1 = its largest), .z = the bin's count.
+__device__ __forceinline__ int3 hist_find(const uint32_t* H, int kk) {
+  const int lane = threadIdx.x & 63;
+  const uint4 h = reinterpret_cast<const uint4*>(H)[lane];
+  const int mine = (int)(h.x + h.y + h.z + h.w);
+  const int inc = wave_inclusive_sum(mine);
+  const int above = __builtin_amdgcn_readlane(inc, 63) - inc;   // entries in higher lanes' bins
+  int d = 0, r = 0, cnt = 0;
+  const bool here = above < kk && kk <= above + mine;
+  if (here) {
+    const int a3 = above + (int)h.w, a2 = a3 + (int)h.z, a1 = a2 + (int)h.y;
+    if (kk <= a3) { d = 3; r = kk - above; cnt = (int)h.w; }
+    else if (kk <= a2) { d = 2; r = kk - a3; cnt = (int)h.z; }
+    else if (kk <= a1) { d = 1; r = kk - a2; cnt = (int)h.y; }
+    else { d = 0; r = kk - a1; cnt = (int)h.x; }
+    d += 4 * lane;
+  }
+  const int src = (int)__ffsll((unsigned long long)__ballot(here)) - 1;
+  return make_int3(__shfl(d, src, 64), __shfl(r, src, 64), __shfl(cnt, src, 64));
+}
+
+// Lower bound of the kk-th largest of the units' keys (0 = no unit): a key that at
+// least kk units reach, and the largest unit.  Every thread returns the same pair.
+// Two barriers.
+template <int U>
+__device__ __forceinline__ uint2 units_lower_bound(const uint32_t (&uk)[U], int kk) {
+  const int tid = threadIdx.x;
+  uint32_t mx = 0u, mn = 0xffffffffu;
+#pragma unroll
+  for (int e = 0; e < U; ++e) {
+    mx = max(mx, uk[e]);
+    mn = min(mn, uk[e] ? uk[e] : 0xffffffffu);
+  }
+  sf.hist[tid] = 0u;
+  const uint2 mm = block_max_min(mx, mn);
+  mx = mm.x;
+  mn = mm.y;
+  if (mx == mn) return make_uint2(mx, mx);   // every unit equal (block-uniform)
+  const float fmn = key_float(mn), fmx = key_float(mx);
+  const float scale = 256.f / (fmx - fmn);
+  if (!(scale > 0.f && scale < 3.0e38f && fmx - fmn < 3.0e38f)) return make_uint2(mn, mx);
+#pragma unroll
+  for (int e = 0; e < U; ++e)
+    if (uk[e]) atomicAdd(&sf.hist[min(255, (int)((key_float(uk[e]) - fmn) * scale))], 1u);
+  __syncthreads();
+  const int bin = hist_find(sf.hist, kk).x;
+  // every unit of the bins from `bin` up lies at or above the edge of bin - 1
+  return make_uint2(bin > 0 ? max(mn, float_key(fmn + (float)(bin - 1) / scale)) : mn, mx);
+}
+
+// The kk-th largest of the keys held by the block (E per thread, 0 = none), all in
+// [lo_key, hi_key].  Radix passes of 8 bits over key - lo_key from the top of the
+// range, one barrier each: the histogram a pass fills was cleared during the
+// previous pass, and it clears the one the next pass fills (rhist[0] is cleared by
+// the caller before an earlier barrier).  A pass whose chosen bin holds a single key
+// ends the search with one more barrier.  Returns (T, how many keys equal to T are
+// kept); the same in every thread.
+template <int E>
+__device__ __forceinline__ uint2 block_select(const uint32_t (&key)[E], uint32_t lo_key,
+                                              uint32_t hi_key, int kk) {
+  const int tid = threadIdx.x;
+  if (hi_key <= lo_key) return make_uint2(hi_key, (uint32_t)kk);
+  int hi = 31 - __clz(hi_key - lo_key);
+  uint32_t prefix = 0u;              // digits of key - lo_key found so far
+  for (int pass = 0;; ++pass) {
+    uint32_t* H = sf.rhist[pass % 3];
+    const int lo = max(hi - 7, 0);
+    const uint32_t pmask = hi == 31 ? 0u : ~((2u << hi) - 1u);
+    const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint32_t r = key[e] - lo_key;
+      if (key[e] && (r & pmask) == prefix) atomicAdd(&H[(r >> lo) & dmask], 1u);
+    }
+    sf.rhist[(pass + 1) % 3][tid] = 0u;
+    __syncthreads();
+    const int3 f = hist_find(H, kk);
+    kk = f.y;
+    prefix |= (uint32_t)f.x << lo;
+    if (lo == 0) return make_uint2(lo_key + prefix, (uint32_t)kk);   // every key of the bin is equal
+    if (f.z == 1) {                  // one key left: its holder publishes it
+      const uint32_t pm = ~((1u << lo) - 1u);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (key[e] && ((key[e] - lo_key) & pm) == prefix) sf.misc[2] = (int)key[e];
+      __syncthreads();
+      return make_uint2((uint32_t)sf.misc[2], 1u);
+    }
+    hi = lo - 1;
+  }
+}
+
+// Kept blocks of a row from its scores in memory, for rows the latency-bound select
+// does not cover (heavy ties, such as a row of equal scores; n > 512): four radix
+// passes of 8 bits over the whole row find T and need_eq exactly, then thread i emits
+// the kept blocks of its contiguous slice of the row at the slots given by a block
+// scan.  Slow but exact for any row; out of line, so that its registers do not add
+// to the latency-bound select's.
+__device__ __attribute__((noinline)) void topk_row_general(
+    int t, const float* __restrict__ scores, int score_stride, const int32_t* __restrict__ q_pos,
+    int32_t* __restrict__ sel_blocks, int32_t* __restrict__ sel_pos, int sel_stride,
+    int32_t* __restrict__ sel_count) {
+  const int tid = threadIdx.x;
+  const float* srow = scores + (size_t)t * score_stride;
+  const int p = q_pos[t];
+  const int n = (p + 1) / kBlock;
+  const int pend = (p + 1) % kBlock;
+  int32_t* row_b = sel_blocks + (size_t)t * kTopK;
+  int32_t* row_p = sel_pos + (size_t)t * sel_stride;
+  uint32_t prefix = 0u;
+  int kk = kTopK;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t pmask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
+    __syncthreads();                   // the previous pass has read the histogram
+    sf.hist[tid] = 0u;
+    __syncthreads();
+    for (int c = tid; c < n; c += kFT) {
+      const uint32_t key = float_key(srow[c]);
+      if ((key & pmask) == prefix) atomicAdd(&sf.hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    const int3 f = hist_find(sf.hist, kk);
+    prefix |= (uint32_t)f.x << shift;
+    kk = f.y;
+  }
+  const uint32_t T = prefix;
+  const int need_eq = kk;
+  const int per = (n + kFT - 1) / kFT;
+  const int cb = min(n, per * tid), ce = min(n, cb + per);
+  int gt = 0, eq = 0;
+  for (int c = cb; c < ce; ++c) {
+    const uint32_t key = float_key(srow[c]);
+    gt += key > T ? 1 : 0;
+    eq += key == T ? 1 : 0;
+  }
+  // (equal counts clamped at 512 keep min(prefix, need_eq) exact and the sums in 17 bits)
+  const uint2 sc = fscan(((uint32_t)min(eq, kTopK) << 10) | (uint32_t)gt);
+  int bgt = (int)(sc.x & 1023u), beq = (int)(sc.x >> 10);
+  for (int c = cb; c < ce; ++c) {
+    const uint32_t key = float_key(srow[c]);
+    int out = -1;
+    if (key > T) {
+      out = bgt + min(beq, need_eq);
+      ++bgt;
+    } else if (key == T) {
+      if (beq < need_eq) out = bgt + beq;
+      ++beq;
+    }
+    if (out >= 0 && out < kTopK) {
+      row_b[out] = c;
+      *reinterpret_cast<int4*>(row_p + kBlock * out) = make_int4(4 * c, 4 * c + 1, 4 * c + 2, 4 * c + 3);
+    }
+  }
+  const int base = kBlock * kTopK;
+  for (int i = base + tid; i < sel_stride; i += kFT) {
+    const int kq = i - base;
+    row_p[i] = kq < pend ? kBlock * n + kq : -1;
+  }
+  if (tid == 0) sel_count[t] = base + pend;
+}
+
+// This thread's float4s of scores (E of them, the first block of each in c[]; -inf
+// or a block past the row = no score) that hold a score >= t0f go to the list.
+template <int E>
+__device__ __forceinline__ void list_float4s(const f32x4_t (&v)[E], const int (&c)[E], float t0f) {
+  bool in[E];
+  int cnt = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    in[e] = fmaxf(fmaxf(v[e][0], v[e][1]), fmaxf(v[e][2], v[e][3])) >= t0f;
+    cnt += in[e] ? 1 : 0;
+  }
+  int slot = wave_slots(cnt, &sf.misc[1]);
+  if (cnt > 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (in[e]) {
+        if (slot < kF4) {
+          sf.lv[slot] = v[e];
+          sf.lc[slot] = c[e];
+        }
+        ++slot;
+      }
+  }
+}
+
+__device__ __forceinline__ void topk_row_fast(int t, const float* __restrict__ scores,
+                                              const float* __restrict__ gmax, int score_stride,
+                                              const int32_t* __restrict__ q_pos,
+                                              int32_t* __restrict__ sel_blocks,
+                                              int32_t* __restrict__ sel_pos, int sel_stride,
+                                              int32_t* __restrict__ sel_count) {
+  const int tid = threadIdx.x;
+  const float* srow = scores + (size_t)t * score_stride;
+  const int gstride = score_stride / kScoreGroup;      // a multiple of 8
+  // this thread's group maxima, requested with the row's position (a thread past the
+  // workspace row reads its last ones)
+  f32x4_t gm4[kGPT / 4];
+  {
+    const float* grow = gmax + (size_t)t * gstride;
+#pragma unroll
+    for (int i = 0; i < kGPT / 4; ++i)
+      gm4[i] = *reinterpret_cast<const f32x4_t*>(grow + min(kGPT * tid + 4 * i, gstride - 4));
+  }
+  const int p = q_pos[t];
+  const int n = (p + 1) / kBlock;
+  QSA_CHECK(p >= 0 && n <= score_stride);
+  const int pend = (p + 1) % kBlock;
+  int32_t* row_b = sel_blocks + (size_t)t * kTopK;
+  int32_t* row_p = sel_pos + (size_t)t * sel_stride;
+  if (n <= kTopK) {
+    for (int i = tid; i < kTopK; i += kFT) row_b[i] = i < n ? i : -1;
+    for (int i = tid; i < sel_stride; i += kFT) row_p[i] = i <= p ? i : -1;
+    if (tid == 0) sel_count[t] = p + 1;
+    return;
+  }
+  // cleared before the first barrier: the select's first histogram, the bitmaps, the
+  // counters
+  sf.rhist[0][tid] = 0u;
+#pragma unroll
+  for (int i = 0; i < kBWT / 4; ++i) {
+    reinterpret_cast<uint4*>(sf.gtb)[kBWT / 4 * tid + i] = make_uint4(0u, 0u, 0u, 0u);
+    reinterpret_cast<uint4*>(sf.eqb)[kBWT / 4 * tid + i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (tid == 0) {
+    sf.misc[0] = 0;
+    sf.misc[1] = 0;
+  }
+  uint32_t t_low, row_max;           // every listed key >= t_low lies in [t_low, row_max]
+  if (n >= kShort) {
+    const int G = (n + kScoreGroup - 1) / kScoreGroup;
+    // ---- lower bound from the group maxima
+    uint32_t uk[kGPT];
+#pragma unroll
+    for (int e = 0; e < kGPT; ++e) uk[e] = kGPT * tid + e < G ? float_key(gm4[e >> 2][e & 3]) : 0u;
+    const uint2 lb = units_lower_bound<kGPT>(uk, kTopK);
+    t_low = max(lb.x, 1u);
+    row_max = lb.y;
+    // ---- candidate groups into LDS (any order)
+    int nc = 0;
+#pragma unroll
+    for (int e = 0; e < kGPT; ++e) nc += uk[e] >= t_low ? 1 : 0;
+    int slot = wave_slots(nc, &sf.misc[0]);
+    if (nc > 0) {
+#pragma unroll
+      for (int e = 0; e < kGPT; ++e)
+        if (uk[e] >= t_low) {
+          if (slot < kFCG) sf.cg[slot] = (uint16_t)(kGPT * tid + e);
+          ++slot;
+        }
+    }
+    __syncthreads();
+    const int ncg = sf.misc[0];
+    if (ncg > kFCG) {                  // heavy ties
+      __syncthreads();
+      topk_row_general(t, scores, score_stride, q_pos, sel_blocks, sel_pos, sel_stride, sel_count);
+      return;
+    }
+    // ---- candidate groups tid, tid + kFT, ..: their scores, as 4 float4s each
+    // (unconditional loads; past the last candidate a thread reads group 0, masked)
+    f32x4_t v[kCGT * 4];
+    int c[kCGT * 4];
+#pragma unroll
+    for (int e = 0; e < kCGT; ++e) {
+      const int i = tid + kFT * e;
+      const int g = i < ncg ? (int)sf.cg[i] : -1;
+      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(srow + kScoreGroup * max(g, 0));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[4 * e + q] = src[q];
+        c[4 * e + q] = g < 0 ? kMaxBlocks : kScoreGroup * g + 4 * q;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kCGT * 4; ++e)
+      if (c[e] >= kMaxBlocks) v[e] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    list_float4s<kCGT * 4>(v, c, key_float(t_low));
+  } else {
+    // ---- short row: the whole row, kSPT blocks per thread in index order
+    const int cs0 = kSPT * tid;
+    f32x4_t v[kSPT / 4];
+    int c[kSPT / 4];
+    uint32_t uk[kSPT / 4];             // quad maxima
+#pragma unroll
+    for (int q = 0; q < kSPT / 4; ++q) {
+      c[q] = cs0 + 4 * q;
+      v[q] = *reinterpret_cast<const f32x4_t*>(srow + min(c[q], score_stride - 4));
+    }
+#pragma unroll
+    for (int q = 0; q < kSPT / 4; ++q) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (c[q] + j >= n) v[q][j] = -INFINITY;
+      const float m = fmaxf(fmaxf(v[q][0], v[q][1]), fmaxf(v[q][2], v[q][3]));
+      uk[q] = c[q] < n ? float_key(m) : 0u;
+    }
+    if ((n + 3) / 4 >= kTopK) {        // at least 512 quads: the 512th largest quad maximum
+      const uint2 lb = units_lower_bound<kSPT / 4>(uk, kTopK);
+      t_low = max(lb.x, 1u);
+      row_max = lb.y;
+    } else {                           // every score is a candidate: the row's range
+      uint32_t mx = 0u, mn = 0xffffffffu;
+#pragma unroll
+      for (int q = 0; q < kSPT / 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (c[q] + j < n) {
+            const uint32_t k = float_key(v[q][j]);
+            mx = max(mx, k);
+            mn = min(mn, k);
+          }
+      const uint2 mm = block_max_min(mx, mn);
+      t_low = max(mm.y, 1u);
+      row_max = mm.x;
+    }
+    list_float4s<kSPT / 4>(v, c, key_float(t_low));
+  }
+  __syncthreads();
+  const int n4 = sf.misc[1];
+  if (n4 > kF4) {                      // heavy ties
+    __syncthreads();
+    topk_row_general(t, scores, score_stride, q_pos, sel_blocks, sel_pos, sel_stride, sel_count);
+    return;
+  }
+
+  // ---- the exact threshold over the listed keys >= t_low; thread i holds float4s
+  // kF4T i .. kF4T i + kF4T - 1
+  uint32_t lk[kF4T * 4];
+  int lc[kF4T];
+#pragma unroll
+  for (int e = 0; e < kF4T; ++e) {
+    const int i = kF4T * tid + e;
+    const f32x4_t x = sf.lv[min(i, kF4 - 1)];
+    lc[e] = sf.lc[min(i, kF4 - 1)];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t k = float_key(x[j]);
+      lk[4 * e + j] = (i < n4 && k >= t_low) ? k : 0u;
+    }
+  }
+  const uint2 thr = block_select<kF4T * 4>(lk, t_low, row_max, kTopK);
+  const uint32_t T = thr.x;
+  const int need_eq = (int)thr.y;
+
+  // ---- mark the blocks above T and those equal to T
+#pragma unroll
+  for (int e = 0; e < kF4T; ++e)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t k = lk[4 * e + j];
+      if (k >= T) {                    // (a key of 0 is below every T)
+        const int cc = lc[e] + j;
+        atomicOr(k > T ? &sf.gtb[cc >> 5] : &sf.eqb[cc >> 5], 1u << (cc & 31));
+      }
+    }
+  __syncthreads();
+
+  // ---- per bitmap word, the blocks above T and equal to T before it (thread i owns
+  // words kBWT i .. kBWT i + kBWT - 1)
+  {
+    uint4 a[kBWT / 4], b[kBWT / 4];
+#pragma unroll
+    for (int i = 0; i < kBWT / 4; ++i) {
+      a[i] = reinterpret_cast<const uint4*>(sf.gtb)[kBWT / 4 * tid + i];
+      b[i] = reinterpret_cast<const uint4*>(sf.eqb)[kBWT / 4 * tid + i];
+    }
+    uint32_t gc[kBWT], ec[kBWT];
+#pragma unroll
+    for (int i = 0; i < kBWT / 4; ++i) {
+      gc[4 * i] = __popc(a[i].x); gc[4 * i + 1] = __popc(a[i].y);
+      gc[4 * i + 2] = __popc(a[i].z); gc[4 * i + 3] = __popc(a[i].w);
+      ec[4 * i] = __popc(b[i].x); ec[4 * i + 1] = __popc(b[i].y);
+      ec[4 * i + 2] = __popc(b[i].z); ec[4 * i + 3] = __popc(b[i].w);
+    }
+    uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+    for (int i = 0; i < kBWT; ++i) {
+      gt += gc[i];
+      eq += ec[i];
+    }
+    // (a set bit is a listed key: at most 4 kF4 of them, so both counts fit 16 bits)
+    const uint2 sc = fscan((eq << 16) | gt);
+    uint32_t rg = sc.x & 0xffffu, re = sc.x >> 16;
+    uint32_t o[kBWT];
+#pragma unroll
+    for (int i = 0; i < kBWT; ++i) {
+      o[i] = (re << 16) | rg;
+      rg += gc[i];
+      re += ec[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kBWT / 4; ++i)
+      reinterpret_cast<uint4*>(sf.pre)[kBWT / 4 * tid + i] =
+          make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+  }
+  __syncthreads();
+  // ---- emit: each kept block goes from the thread that holds its key to slot (above
+  // before it) + min(equal before it, need_eq); a block equal to T is kept while fewer
+  // than need_eq equal blocks precede it
+#pragma unroll
+  for (int e = 0; e < kF4T; ++e)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t k = lk[4 * e + j];
+      if (k >= T) {
+        const int cc = lc[e] + j;
+        const int w = cc >> 5;
+        const uint32_t below = (1u << (cc & 31)) - 1u;
+        const uint32_t pw = sf.pre[w];
+        const int g_below = (int)(pw & 0xffffu) + __popc(sf.gtb[w] & below);
+        const int e_below = (int)(pw >> 16) + __popc(sf.eqb[w] & below);
+        int out = -1;
+        if (k > T) out = g_below + min(e_below, need_eq);
+        else if (e_below < need_eq) out = g_below + e_below;
+        if (out >= 0 && out < kTopK) {   // exactly kTopK are kept; the guard bounds the row
+          row_b[out] = cc;
+          *reinterpret_cast<int4*>(row_p + kBlock * out) =
+              make_int4(4 * cc, 4 * cc + 1, 4 * cc + 2, 4 * cc + 3);
+        }
+      }
+    }
+  const int base = kBlock * kTopK;
+  for (int i = base + tid; i < sel_stride; i += kFT) {
+    const int kq = i - base;
+    row_p[i] = kq < pend ? kBlock * n + kq : -1;
+  }
+  if (tid == 0) sel_count[t] = base + pend;
+}
+
+__global__ void __launch_bounds__(kFT)
+topk_kernel(const float* __restrict__ scores, const float* __restrict__ gmax, int score_stride,
             const int32_t* __restrict__ q_pos, int32_t* __restrict__ sel_blocks,
             int32_t* __restrict__ sel_pos, int sel_stride, int32_t* __restrict__ sel_count) {
-  topk_row(blockIdx.x, scores, score_stride, gmax, q_pos, sel_blocks, sel_pos, sel_stride, sel_count);
+  topk_row_fast(blockIdx.x, scores, gmax, score_stride, q_pos, sel_blocks, sel_pos, sel_stride,
+                sel_count);
 }
 
 // The rows listed in queue[1 .. queue[0]] (rows the code-based select hands over).
@@ -556,16 +1096,14 @@ topk_queued_kernel(const int* __restrict__ queue, const float* __restrict__ scor
 }  // namespace
 
 void launch_topk(const IndexArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(topk_kernel, dim3(a.total_q), dim3(kT), 0, stream, a.scores, a.score_stride,
-                     a.gmax_f, a.q_pos, a.sel_blocks, a.sel_pos, a.sel_stride, a.sel_count);
-  note_launch(stream);
+  QSA_LAUNCH(topk_kernel, dim3(a.total_q), dim3(kFT), 0, stream, a.scores, a.gmax_f, a.score_stride,
+             a.q_pos, a.sel_blocks, a.sel_pos, a.sel_stride, a.sel_count);
 }
 
 void launch_topk_queued(const IndexArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(topk_queued_kernel, dim3(std::min(a.total_q, 256)), dim3(kT), 0, stream, a.queue,
+  QSA_LAUNCH(topk_queued_kernel, dim3(std::min(a.total_q, 256)), dim3(kT), 0, stream, a.queue,
                      a.scores, a.score_stride, a.q_pos, a.sel_blocks, a.sel_pos, a.sel_stride,
                      a.sel_count);
-  note_launch(stream);
 }
 
 }  // namespace qsa

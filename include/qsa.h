@@ -92,18 +92,19 @@ enum qsa_op {
 const char* qsa_status_string(int status);
 
 /* Profiling aid: the calling thread's next QSA call (any entry point below)
- * records events[i] on its stream right after launching its i-th kernel, for i <
- * n_events and as many kernels as it launches; then the request lapses.  With it a
- * caller times each kernel of a multi-kernel call with HIP events (event i minus
- * event i-1, or minus an event recorded before the call).  events: n_events
- * hipEvent_t handles created by the caller (host array).  n_events in 0..8 (0
- * cancels), else QSA_E_SHAPE; a NULL handle gives QSA_E_NULL.  It changes no
- * result.  The kernels a call launches, in order: qsa_decode_build_index_topk: the
- * scorer (builder folded in), then the select; qsa_index_topk: the scorer (one
- * launch per 64 queries, or per 256 queries of the multi-query scorer, in decode
- * and verification batches), then the select, and for prefill chunks the MFMA
- * scorer, the code select, the exact rescoring and the queued select; the sparse
- * GQA calls: the gather, then the split combine when the list is split. */
+ * launches its i-th kernel with the start and stop events events[2i] and
+ * events[2i+1] (hipExtLaunchKernelGGL: the runtime sets them from the dispatch's own
+ * start and end timestamps, so their elapsed time is the kernel's duration), for i <
+ * n_events / 2 and as many kernels as the call launches; then the request lapses.
+ * events: n_events hipEvent_t handles created by the caller (host array).  n_events
+ * even, 0..16 (0 cancels), else QSA_E_SHAPE; a NULL handle gives QSA_E_NULL.  It
+ * changes no result.  The kernels a call launches, in order:
+ * qsa_decode_build_index_topk: the scorer (builder folded in), then the select;
+ * qsa_index_topk: the scorer (one launch per 64 queries, or per 256 queries of the
+ * multi-query scorer, in decode and verification batches), then the select, and for
+ * prefill chunks the MFMA scorer, the code select, the exact rescoring and the queued
+ * select; the sparse GQA calls: the gather, then the split combine when the list is
+ * split; the builders: one kernel. */
 int qsa_profile_kernel_events(void* const* events, int32_t n_events);
 
 /* Workspace bytes that `op` needs for `total_q` queries.

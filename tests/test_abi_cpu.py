@@ -224,16 +224,18 @@ def test_gqa_noalloc_validation():
 
 def test_profile_kernel_events_validation():
     L = B.lib()
-    ev = (ctypes.c_void_p * 9)(*([FAKE] * 9))
-    assert L.qsa_profile_kernel_events(ev, 9) == B.QSA_E_SHAPE
-    assert L.qsa_profile_kernel_events(ev, -1) == B.QSA_E_SHAPE
+    ev = (ctypes.c_void_p * 18)(*([FAKE] * 18))
+    assert L.qsa_profile_kernel_events(ev, 18) == B.QSA_E_SHAPE     # at most 8 kernels
+    assert L.qsa_profile_kernel_events(ev, 3) == B.QSA_E_SHAPE      # (start, stop) pairs
+    assert L.qsa_profile_kernel_events(ev, -2) == B.QSA_E_SHAPE
     assert L.qsa_profile_kernel_events(None, 2) == B.QSA_E_NULL
     ev[1] = None
     assert L.qsa_profile_kernel_events(ev, 2) == B.QSA_E_NULL
     assert L.qsa_profile_kernel_events(None, 0) == B.QSA_OK        # cancels
-    # a request lapses with the next call, even one that fails validation and records
-    # nothing (otherwise a later call would record into events the caller dropped)
-    assert L.qsa_profile_kernel_events(ev, 1) == B.QSA_OK
+    # a request lapses with the next call, even one that fails validation and launches
+    # nothing (otherwise a later call would set events the caller dropped)
+    ev[1] = FAKE
+    assert L.qsa_profile_kernel_events(ev, 2) == B.QSA_OK
     d = B.default_dims()
     assert L.qsa_sparse_gqa_decode(ctypes.byref(d), 8, None, FAKE, FAKE, FAKE, 64, FAKE, FAKE, 2052,
                                    None, 0, FAKE, None, FAKE, 1 << 30, None) == B.QSA_E_NULL

@@ -9,6 +9,7 @@ import sys
 import types
 
 import numpy as np
+import pytest
 
 import bench
 
@@ -49,13 +50,47 @@ def test_traffic_reported_only_for_unchanged_sources(tmp_path, monkeypatch):
     src = tmp_path / "kernel.hip"
     src.write_text("// kernel v1\n")
     rec = tmp_path / "traffic.json"
-    monkeypatch.setitem(bench.KERNEL_SOURCES, "attend", [str(src)])
+    monkeypatch.setitem(bench.KERNEL_SOURCES, "attn_kernel", [str(src)])
     monkeypatch.setattr(bench, "traffic_file", lambda workload: str(rec))
     monkeypatch.setattr(bench, "ROOT", "/")
-    rec.write_text(json.dumps({"attend": {"bytes_per_launch": 12345,
-                                          "source_hash": bench.source_hash([str(src)])}}))
-    assert bench.load_traffic("w", "attend") == 12345
+    rec.write_text(json.dumps({"attn_kernel": {"bytes_per_launch": 12345,
+                                               "source_hash": bench.source_hash([str(src)])}}))
+    assert bench.load_traffic("w", "attn_kernel") == 12345
     src.write_text("// kernel v2\n")
-    assert bench.load_traffic("w", "attend") is None
+    assert bench.load_traffic("w", "attn_kernel") is None
     rec.unlink()
-    assert bench.load_traffic("w", "attend") is None
+    assert bench.load_traffic("w", "attn_kernel") is None
+
+
+def test_every_kernel_has_its_sources():
+    for k in ("attn_kernel", "combine_kernel", "score_build_kernel", "score_kernel", "score_multi_kernel",
+              "topk_kernel", "score_mfma_kernel", "topk_codes_kernel", "build_kernel"):
+        for pth in bench.KERNEL_SOURCES[k]:
+            assert os.path.exists(os.path.join(ROOT, pth)), pth
+
+
+def test_attention_bytes_split_between_gather_and_combine():
+    got = bench.attend_kernel_bytes(10_000_000, 32, combined=True)
+    out = 32 * (16 * 256 * 2 + 16 * 4)
+    assert got == {"attn_kernel": 10_000_000 - out, "combine_kernel": out}
+    assert bench.attend_kernel_bytes(10_000_000, 32, combined=False) == {"attn_kernel": 10_000_000}
+
+
+@pytest.mark.parametrize("kind", ["decode", "prefill", "indexshare"])
+def test_oracle_baseline_over_worker_processes(kind):
+    # the CPU baseline's machinery on a small workload: spawned workers map the staged
+    # inputs and run the oracle's units; the report names the cores it used
+    from block_sparse_attention_c4_amd import synth
+    if kind == "prefill":
+        wl = synth.make_workload("pool_pf", "prefill", 41, [3000], chunk=6)
+    elif kind == "indexshare":
+        wl = synth.make_workload("pool_is", "indexshare", 42, [2600, 1203], reuse_steps=3)
+    else:
+        wl = synth.make_workload("pool_dec", "decode", 43, [2600, 1203, 5000])
+    b = bench.OracleBaseline(2)
+    try:
+        r = b.run(wl, seconds=0.5, seconds_single=0.2)
+    finally:
+        b.close()
+    assert r["cores"] == 2 and r["kind"] == "oracle" and r["value"] > 0
+    assert r["single_thread"]["cores"] == 1 and r["single_thread"]["value"] > 0
