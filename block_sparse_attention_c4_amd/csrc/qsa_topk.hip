@@ -534,11 +534,12 @@ __device__ __forceinline__ void topk_row(int t, const float* __restrict__ scores
 
 // ------------------------------------------------------------------ latency-bound select
 
-// The select of topk_kernel: one work group of kFT threads per row.  A row's time is
-// a chain of dependent steps, each a few hundred instructions per wave plus a
-// barrier; every instruction of a wave costs the SIMD it shares with the other waves,
-// so the group is kept to kFT = 256 threads (one wave per SIMD), and the work on the
-// row's scores is done four scores at a time.
+// The select of topk_kernel: one work group of kFT = 1024 threads per row.  A row's
+// time is a chain of dependent steps (two memory round trips, then LDS work with a
+// barrier after each step).  With 16 waves, 4 per SIMD, each wave holds only a few of
+// the row's units per step and the waves of a SIMD hide each other's LDS and memory
+// latency (batch 32: 9.6 us per launch against 11.2 with 512 threads and 15.0 with
+// 256).  The work on the row's scores is done four scores at a time.
 //   - The row's position and its 16-block group maxima (written by the scorer) are
 //     requested together at kernel start, the maxima before the row's length is known
 //     (the workspace row of maxima is score_stride / 16 long), so the first memory
@@ -564,19 +565,19 @@ __device__ __forceinline__ void topk_row(int t, const float* __restrict__ scores
 // 512 quads): with so few groups the 512th group maximum keeps most groups, and their
 // float4s above it can overflow the list.  Rows with too many candidates (heavy ties,
 // such as a row of equal scores) take an exact select over the row in memory.
-constexpr int kFT = 256;                          // threads per row
+constexpr int kFT = 1024;                         // threads per row
 constexpr int kFW = kFT / 64;
-constexpr int kGPT = kMaxBlocks / kScoreGroup / kFT;   // group maxima per thread: 16
+constexpr int kGPT = kMaxBlocks / kScoreGroup / kFT;   // group maxima per thread: 4
 constexpr int kFCG = 1024;                        // candidate groups
-constexpr int kCGT = kFCG / kFT;                  // candidate groups per thread: 4
+constexpr int kCGT = kFCG / kFT;                  // candidate groups per thread: 1
 constexpr int kShort = 2 * kTopK * kScoreGroup;   // rows below this many blocks are short
-constexpr int kSPT = kShort / kFT;                // short-row scores per thread: 64
+constexpr int kSPT = kShort / kFT;                // short-row scores per thread: 16
 constexpr int kF4 = 1024;                         // listed float4s
-constexpr int kF4T = kF4 / kFT;                   // listed float4s per thread: 4
+constexpr int kF4T = kF4 / kFT;                   // listed float4s per thread: 1
 constexpr int kBWords = kMaxBlocks / 32;          // bitmap words: 2048
-constexpr int kBWT = kBWords / kFT;               // bitmap words per thread: 8
-static_assert(kGPT % 4 == 0 && kSPT % 4 == 0 && kBWT % 4 == 0, "whole 16-byte accesses");
-static_assert(kFT >= 256, "one histogram bin per thread");
+constexpr int kBWT = kBWords / kFT;               // bitmap words per thread: 2
+static_assert(kGPT % 4 == 0 && kSPT % 4 == 0, "whole 16-byte accesses");
+static_assert(kFT >= 256 && kFT <= 1024 && kBWT >= 1, "256-bin histograms, one bin per thread");
 static_assert(4 * kF4 < 65536, "bitmap counts packed in 16 bits");
 
 struct __attribute__((aligned(16))) SmemF {
@@ -674,7 +675,7 @@ __device__ __forceinline__ uint2 units_lower_bound(const uint32_t (&uk)[U], int 
     mx = max(mx, uk[e]);
     mn = min(mn, uk[e] ? uk[e] : 0xffffffffu);
   }
-  sf.hist[tid] = 0u;
+  if (tid < 256) sf.hist[tid] = 0u;
   const uint2 mm = block_max_min(mx, mn);
   mx = mm.x;
   mn = mm.y;
@@ -715,7 +716,7 @@ __device__ __forceinline__ uint2 block_select(const uint32_t (&key)[E], uint32_t
       const uint32_t r = key[e] - lo_key;
       if (key[e] && (r & pmask) == prefix) atomicAdd(&H[(r >> lo) & dmask], 1u);
     }
-    sf.rhist[(pass + 1) % 3][tid] = 0u;
+    if (tid < 256) sf.rhist[(pass + 1) % 3][tid] = 0u;
     __syncthreads();
     const int3 f = hist_find(H, kk);
     kk = f.y;
@@ -756,7 +757,7 @@ __device__ __attribute__((noinline)) void topk_row_general(
     const int shift = 24 - 8 * pass;
     const uint32_t pmask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
     __syncthreads();                   // the previous pass has read the histogram
-    sf.hist[tid] = 0u;
+    if (tid < 256) sf.hist[tid] = 0u;
     __syncthreads();
     for (int c = tid; c < n; c += kFT) {
       const uint32_t key = float_key(srow[c]);
@@ -860,11 +861,11 @@ __device__ __forceinline__ void topk_row_fast(int t, const float* __restrict__ s
   }
   // cleared before the first barrier: the select's first histogram, the bitmaps, the
   // counters
-  sf.rhist[0][tid] = 0u;
+  if (tid < 256) sf.rhist[0][tid] = 0u;
 #pragma unroll
-  for (int i = 0; i < kBWT / 4; ++i) {
-    reinterpret_cast<uint4*>(sf.gtb)[kBWT / 4 * tid + i] = make_uint4(0u, 0u, 0u, 0u);
-    reinterpret_cast<uint4*>(sf.eqb)[kBWT / 4 * tid + i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = 0; i < kBWT; ++i) {
+    sf.gtb[kBWT * tid + i] = 0u;
+    sf.eqb[kBWT * tid + i] = 0u;
   }
   if (tid == 0) {
     sf.misc[0] = 0;
@@ -1002,19 +1003,11 @@ __device__ __forceinline__ void topk_row_fast(int t, const float* __restrict__ s
   // ---- per bitmap word, the blocks above T and equal to T before it (thread i owns
   // words kBWT i .. kBWT i + kBWT - 1)
   {
-    uint4 a[kBWT / 4], b[kBWT / 4];
-#pragma unroll
-    for (int i = 0; i < kBWT / 4; ++i) {
-      a[i] = reinterpret_cast<const uint4*>(sf.gtb)[kBWT / 4 * tid + i];
-      b[i] = reinterpret_cast<const uint4*>(sf.eqb)[kBWT / 4 * tid + i];
-    }
     uint32_t gc[kBWT], ec[kBWT];
 #pragma unroll
-    for (int i = 0; i < kBWT / 4; ++i) {
-      gc[4 * i] = __popc(a[i].x); gc[4 * i + 1] = __popc(a[i].y);
-      gc[4 * i + 2] = __popc(a[i].z); gc[4 * i + 3] = __popc(a[i].w);
-      ec[4 * i] = __popc(b[i].x); ec[4 * i + 1] = __popc(b[i].y);
-      ec[4 * i + 2] = __popc(b[i].z); ec[4 * i + 3] = __popc(b[i].w);
+    for (int i = 0; i < kBWT; ++i) {
+      gc[i] = __popc(sf.gtb[kBWT * tid + i]);
+      ec[i] = __popc(sf.eqb[kBWT * tid + i]);
     }
     uint32_t gt = 0u, eq = 0u;
 #pragma unroll
@@ -1033,9 +1026,7 @@ __device__ __forceinline__ void topk_row_fast(int t, const float* __restrict__ s
       re += ec[i];
     }
 #pragma unroll
-    for (int i = 0; i < kBWT / 4; ++i)
-      reinterpret_cast<uint4*>(sf.pre)[kBWT / 4 * tid + i] =
-          make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+    for (int i = 0; i < kBWT; ++i) sf.pre[kBWT * tid + i] = o[i];
   }
   __syncthreads();
   // ---- emit: each kept block goes from the thread that holds its key to slot (above
