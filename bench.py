@@ -611,6 +611,9 @@ def main() -> int:
                          "qsa_decode_build_index_topk call does both)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one elementwise kernel over this size (counter calibration)")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the shorter runs of the other workloads reported under "
+                         "other_workloads (also skipped with --headline-only)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -637,12 +640,70 @@ def main() -> int:
 
 def run(args, cfg, kind, steps, warmup, nsets, K, baseline) -> int:
     import torch
-    from block_sparse_attention_c4_amd import runner, synth
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     torch.cuda.set_device(0)
+    result, wl, kv = measure(args, args.workload, steps, warmup, nsets, K)
+    if not args.no_ceilings:
+        result["measured_ceilings"] = measured_ceilings(torch)
+        if "step_hbm_gbps" in result:
+            result["step_frac_of_measured_copy"] = round(
+                result["step_hbm_gbps"] / result["measured_ceilings"]["stream_copy_gbps"], 4)
+    if baseline is not None:
+        result["cpu_baseline"] = baseline.run(wl, args.cpu_seconds, args.cpu_seconds_single, kv)
+        result["cpu_baseline"]["host"] = host_cpu()
+    del wl
+    if not (args.headline_only or args.no_others):
+        result["other_workloads"] = other_workloads(args, torch)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+OTHER_SUMMARY_KEYS = ("metric", "value", "unit", "ms_per_step", "steps", "warmup", "kernel_us",
+                      "ms_per_step_without_reuse", "tokens_per_s_without_reuse", "reuse_kernel_us",
+                      "step_hbm_frac", "stage_tflops")
+
+
+def other_workloads(args, torch) -> dict:
+    """Every other workload, timed the same way with a quarter of its steps: the whole
+    step through hipGraph replays, per-kernel HIP events, and the roofline of its
+    dominant kernel."""
+    import copy
+    import gc
+
+    out = {}
+    sub = copy.copy(args)
+    sub.headline_only = True
+    sub.projection_overlap = 0
+    sub.calib_copy_mib = 0
+    for name, cfg in WORKLOADS.items():
+        if name == args.workload:
+            continue
+        steps = max(10, cfg["steps"] // 4)
+        warmup = max(2, cfg["warmup"] // 2)
+        t0 = time.time()
+        r, _, _ = measure(sub, name, steps, warmup, cfg["sets"], min(100, steps))
+        summary = {k: r[k] for k in OTHER_SUMMARY_KEYS if k in r}
+        rf = r["roofline"]
+        summary["roofline"] = {k: rf[k] for k in ("bound", "kernel", "achieved", "peak", "unit", "frac")}
+        summary["wall_s"] = round(time.time() - t0, 1)
+        out[name] = summary
+        del r
+        gc.collect()
+        torch.cuda.empty_cache()
+    return out
+
+
+def measure(args, name, steps, warmup, nsets, K):
+    """One workload: returns (result line without ceilings or CPU baseline, the
+    workload, its K/V format)."""
+    import torch
+    from block_sparse_attention_c4_amd import runner, synth
+
+    cfg = WORKLOADS[name]
+    kind = cfg["kind"]
     kv = cfg.get("kv", "bf16")
-    wl = synth.FULL_SIZE[cfg.get("source", args.workload)]()
+    wl = synth.FULL_SIZE[cfg.get("source", name)]()
     if kv == "fp8":
         synth.with_fp8_kv(wl)
     base = runner.DeviceWorkload(wl, "cuda:0", kv=kv)
@@ -765,7 +826,7 @@ def run(args, cfg, kind, steps, warmup, nsets, K, baseline) -> int:
         torch.mul(a, 1.0, out=b)
         torch.cuda.synchronize()
 
-    config = {"workload": args.workload, "batch": wl.batch, "seed": wl.seed, "context": cfg["context"],
+    config = {"workload": name, "batch": wl.batch, "seed": wl.seed, "context": cfg["context"],
               "q_heads": 16, "kv_heads": 2, "head_dim": 256, "indexer": "4x128", "topk_blocks": 512,
               "page_size": wl.page_size, "input_sets": len(sets), "launch": launch}
     if kv == "fp8":
@@ -803,7 +864,7 @@ def run(args, cfg, kind, steps, warmup, nsets, K, baseline) -> int:
         achieved = nbytes_kernel / (us * 1e-6) / 1e9
         return {"bound": "hbm", "kernel": kernel, "entry_point": entry, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": load_traffic(args.workload, kernel), "bytes_per_launch": int(nbytes_kernel),
+                "traffic": load_traffic(name, kernel), "bytes_per_launch": int(nbytes_kernel),
                 "kernel_us": round(us, 2),
                 "how": "algorithmic bytes of one launch over the kernel's mean duration from HIP events "
                        "(kernel_us)"}
@@ -824,7 +885,7 @@ def run(args, cfg, kind, steps, warmup, nsets, K, baseline) -> int:
         result["roofline"] = {"bound": "mfma", "kernel": "score_mfma_kernel", "entry_point": ENTRY["index"],
                               "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                              "traffic": load_traffic(args.workload, "score_mfma_kernel"),
+                              "traffic": load_traffic(name, "score_mfma_kernel"),
                               "flops_per_launch": work["score_flops"], "kernel_us": round(us, 2),
                               "how": "the scorer's FLOPs (4 heads x 128 dims x 2 per visible block of "
                                      "every query) over its mean duration from HIP events; "
@@ -868,17 +929,7 @@ def run(args, cfg, kind, steps, warmup, nsets, K, baseline) -> int:
         split = attend_kernel_bytes(nbytes["attend"], wl.batch, combined)
         entry = "qsa_sparse_gqa_decode_fp8" if kv == "fp8" else ENTRY["attend"]
         result["roofline"] = hbm_roofline("attn_kernel", entry, split["attn_kernel"], stage_us["attn_kernel"])
-
-    if not args.no_ceilings:
-        result["measured_ceilings"] = measured_ceilings(torch)
-        if "step_hbm_gbps" in result:
-            result["step_frac_of_measured_copy"] = round(
-                result["step_hbm_gbps"] / result["measured_ceilings"]["stream_copy_gbps"], 4)
-    if baseline is not None:
-        result["cpu_baseline"] = baseline.run(wl, args.cpu_seconds, args.cpu_seconds_single, kv)
-        result["cpu_baseline"]["host"] = host_cpu()
-    print(json.dumps(result), flush=True)
-    return 0
+    return result, wl, kv
 
 
 if __name__ == "__main__":
