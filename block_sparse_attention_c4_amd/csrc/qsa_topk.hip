@@ -5,29 +5,29 @@
 // their 2048 token positions, and the 0..3 tokens of the unfinished block are
 // appended.  Ties go to the lower block index; kept blocks are listed ascending.
 //
-// One 1024-thread work group per query, on an order-preserving 32-bit key of each
-// FP32 score.  With one work group per query the kernel is bound by the length of a
-// thread's instruction stream, so the work is spread over 16 waves and every score
-// of the row is read once, as float4 quads kept in registers (at most 16 quads per
-// thread for 65536 blocks).
-//
-//  1. n <= 512: every block is kept.
-//  2. Lower bound: the 512th largest quad maximum t0 (found to 16 bits below the
-//     keys' common prefix, rounded down) has at least 512 quads, hence 512 scores,
-//     at or above it.  (Skipped when n <= 4096: t0 = 0.)  Rows of more than 4096
-//     blocks use the scorer's 16-block group maxima instead and read only the
-//     groups whose maximum reaches the bound.
-//  3. Scores >= t0 go to LDS as candidates (a block-wide prefix count gives their
-//     slots); typically a thousand or fewer.
-//  4. Exact radix select over the candidates: the threshold key and how many keys
-//     equal to it are kept (ties go to the lowest block indices).
-//  5. Kept blocks are marked in an LDS bitmap and written in index order from a
-//     per-word prefix count.
-// Radix passes use 8-bit digits that start at the first bit where the keys' max
-// and min differ; one wave scans the 256-bin histogram while the other waves clear
-// the next one.  More than kCap candidates (heavy ties) falls back to a select over
-// the score row in global memory.  topk_queued_kernel runs the same select for the
-// rows that the code-based select of qsa_prefill.hip hands over.
+// Two selects, both on an order-preserving 32-bit key of each FP32 score and one
+// 1024-thread work group per query row:
+//   - topk_kernel (decode, verification, the indexer's general path): the
+//     latency-bound select described before it below.  It starts from the scorer's
+//     16-block group maxima and reads only the candidate groups of a long row.
+//   - topk_row, used by topk_queued_kernel for the rows that the code-based prefill
+//     select of qsa_prefill.hip hands over (heavy ties): every score of the row is read
+//     once, as float4 quads kept in registers (at most 16 quads per thread for 65536
+//     blocks).
+//      1. n <= 512: every block is kept.
+//      2. Lower bound: the 512th largest quad maximum t0 (found to 16 bits below the
+//         keys' common prefix, rounded down) has at least 512 quads, hence 512 scores,
+//         at or above it.  (Skipped when n <= 4096: t0 = 0.)
+//      3. Scores >= t0 go to LDS as candidates (a block-wide prefix count gives their
+//         slots); typically a thousand or fewer.
+//      4. Exact radix select over the candidates: the threshold key and how many keys
+//         equal to it are kept (ties go to the lowest block indices).
+//      5. Kept blocks are marked in an LDS bitmap and written in index order from a
+//         per-word prefix count.
+//     Radix passes use 8-bit digits that start at the first bit where the keys' max
+//     and min differ; one wave scans the 256-bin histogram while the other waves
+//     clear the next one.  More than kCap candidates falls back to a select over the
+//     score row in global memory.
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
