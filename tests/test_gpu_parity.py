@@ -277,6 +277,16 @@ def test_index_all_ties():
     _check_index_stage(wl, exact=True)
 
 
+def test_index_all_ties_long_rows():
+    # every score 0 on rows long enough for the group-maxima path: exactly 1024 groups
+    # (every group a candidate, whose float4s overflow the list), 1094 groups (more
+    # candidate groups than the list of groups holds) and 2048 groups; each row falls
+    # back to the exact select over the row in memory and keeps the 512 lowest blocks
+    wl = synth.make_workload("ties_long", "decode", 317, [65539, 70000, 131072])
+    wl.idx_q[:] = 0
+    _check_index_stage(wl, exact=True)
+
+
 def test_index_zero_keys_tie_break():
     # all-zero raw keys: every compressed key is zero (the norm floor), every score
     # is 0, and the 512 lowest block indices are kept
