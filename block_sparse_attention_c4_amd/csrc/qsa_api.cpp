@@ -73,12 +73,12 @@ const char* qsa_status_string(int status) {
 }
 
 int qsa_profile_kernel_events(void* const* events, int32_t n_events) {
+  t_profile.n = t_profile.next = 0;   // a rejected request also cancels an earlier one
   if (n_events < 0 || n_events > kMaxProfileEvents || n_events % 2 != 0) return QSA_E_SHAPE;
   if (n_events > 0 && !events) return QSA_E_NULL;
-  for (int i = 0; i < n_events; ++i) {
+  for (int i = 0; i < n_events; ++i)
     if (!events[i]) return QSA_E_NULL;
-    t_profile.ev[i] = static_cast<hipEvent_t>(events[i]);
-  }
+  for (int i = 0; i < n_events; ++i) t_profile.ev[i] = static_cast<hipEvent_t>(events[i]);
   t_profile.n = n_events;
   t_profile.next = 0;
   return QSA_OK;
@@ -121,6 +121,7 @@ int qsa_build_index_keys_mrope(const qsa_dims* dims, int32_t batch, const uint16
                                const int32_t* page_table, int32_t pt_stride,
                                const uint8_t* pair_axis, uint16_t* ring, int32_t* ring_mpos,
                                uint16_t* comp_cache, void* stream) {
+  CallScope scope;
   if (!pair_axis) return QSA_E_NULL;
   for (int i = 0; i < 64; ++i)
     if (pair_axis[i] > 2) return QSA_E_SHAPE;
@@ -275,6 +276,7 @@ int qsa_decode_build_index_topk_mrope(const qsa_dims* dims, int32_t batch,
                                       const float* idx_w, int32_t* sel_blocks, int32_t* sel_pos,
                                       int32_t sel_stride, int32_t* sel_count, void* workspace,
                                       size_t ws_bytes, void* stream) {
+  CallScope scope;
   if (!pair_axis || !new_mpos || !ring_mpos) return QSA_E_NULL;
   for (int i = 0; i < 64; ++i)
     if (pair_axis[i] > 2) return QSA_E_SHAPE;

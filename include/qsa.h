@@ -95,9 +95,10 @@ const char* qsa_status_string(int status);
  * launches its i-th kernel with the start and stop events events[2i] and
  * events[2i+1] (hipExtLaunchKernelGGL: the runtime sets them from the dispatch's own
  * start and end timestamps, so their elapsed time is the kernel's duration), for i <
- * n_events / 2 and as many kernels as the call launches; then the request lapses.
- * events: n_events hipEvent_t handles created by the caller (host array).  n_events
- * even, 0..16 (0 cancels), else QSA_E_SHAPE; a NULL handle gives QSA_E_NULL.  It
+ * n_events / 2 and as many kernels as the call launches; then the request lapses
+ * (also when that call returns an error).  events: n_events hipEvent_t handles created
+ * by the caller (host array).  n_events even, 0..16 (0 cancels), else QSA_E_SHAPE; a
+ * NULL handle gives QSA_E_NULL; a rejected request also cancels an earlier one.  It
  * changes no result.  The kernels a call launches, in order:
  * qsa_decode_build_index_topk: the scorer (builder folded in), then the select;
  * qsa_index_topk: the scorer (one launch per 64 queries, or per 256 queries of the
