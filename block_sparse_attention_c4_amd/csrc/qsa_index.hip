@@ -7,10 +7,16 @@
 // s_c = sum_h w_h * max(0, q_h . k_c) over the 4 indexer heads.
 //
 // score_kernel is a paged GEMV.  A wave streams groups of 16 consecutive blocks
-// (one 4 KB compressed page when page_size = 64): 4 loads of 16 B per lane, each
-// load covering 4 blocks x 256 B contiguous.  Lane l owns dims (l%16)*8 .. +8 of
-// block (l/16); the dot products use v_dot2_f32_bf16 (bf16 pairs, FP32
-// accumulation) and are summed over the 16 lanes of a row with DPP.
+// (one 4 KB compressed page when page_size = 64): 4 loads of 16 B per lane.  The
+// dot products run on v_mfma_f32_16x16x32_bf16 with the group's keys as the B
+// operand (lane l holds block l%16, dims 8(l/16) + 32kc of K-chunk kc, so a load
+// covers 64 contiguous bytes of each of the 16 rows) and the query's 4 heads as rows
+// 0..3 of the A operand (rows 4..15 zero): four MFMAs leave the 4 head dots of block
+// l in lane l < 16, which mixes them with head_mix, the arithmetic of every MFMA
+// scorer.  The MFMA's idle rows cost nothing that matters here; against the
+// v_dot2_f32_bf16 form with DPP row sums it replaces about 160 VALU instructions per
+// group by 4 MFMAs and 8 VALU, and the batch-32 decode scorer went from 20.2 to
+// 17.7 us.
 //
 // score_multi_kernel serves batches with a few queries per request, such as the
 // verification pass over drafted tokens [same post, section "IndexShare MTP:
@@ -28,11 +34,8 @@ namespace qsa {
 namespace {
 
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
 __device__ __forceinline__ int groups_of(int p) {
@@ -68,7 +71,7 @@ struct GroupMeta {
 };
 
 struct QueryRows {
-  u32x4_t qf[kIdxHeads];
+  u32x4_t af[4];         // A operand: head l%16 (rows 4..15 zero), dims 8(l/16) + 32kc
   float w[kIdxHeads];
 };
 
@@ -109,8 +112,6 @@ __device__ __forceinline__ void score_body(
   const int excl = incl - my_groups;
   const int total = __shfl(incl, 63, 64);
 
-  const int d0 = (lane & 15) * 8;
-  const int row_in_step = lane >> 4;
   const int bpp = page_size / kBlock;
   int g_begin = 0;
   int ng = 0;
@@ -124,49 +125,39 @@ __device__ __forceinline__ void score_body(
     m.pt_row = page_table + (size_t)__shfl(my_req, m.t, 64) * pt_stride;
     return m;
   };
-  auto block_of = [&](const GroupMeta& m, int r) {
-    return min(m.g * kScoreGroup + 4 * r + row_in_step, m.n_c - 1);
-  };
-  auto pt_load = [&](int i, int (&pg)[4]) {
+  // lane l holds block l%16 of a group as the B operand, dims 8(l/16) + 32kc
+  auto block_of = [&](const GroupMeta& m) { return min(m.g * kScoreGroup + (lane & 15), m.n_c - 1); };
+  auto pt_load = [&](int i) {
     const GroupMeta m = meta(i);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pg[r] = m.pt_row[block_of(m, r) / bpp];
-      QSA_CHECK(pg[r] >= 0);
-    }
+    const int pg = m.pt_row[block_of(m) / bpp];
+    QSA_CHECK(pg >= 0);
+    return pg;
   };
-  auto key_load = [&](int i, const int (&pg)[4], u32x4_t (&kv)[4]) {
+  auto key_load = [&](int i, int pg, u32x4_t (&kv)[4]) {
     const GroupMeta m = meta(i);
     if (lane == 0) s_tg[i] = (m.t << 16) | m.g;
+    const int c = block_of(m);
+    const uint16_t* krow = comp + ((int64_t)pg * bpp + (c % bpp)) * kIdxDim + 8 * (lane >> 4);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int c = block_of(m, r);
-      const int64_t row = (int64_t)pg[r] * bpp + (c % bpp);
-      kv[r] = ld16(comp + row * kIdxDim + d0);
-    }
+    for (int kc = 0; kc < 4; ++kc) kv[kc] = ld16(krow + 32 * kc);
   };
   auto query_load = [&](int t, QueryRows& q) {
+    const int h = lane & 15;
 #pragma unroll
-    for (int h = 0; h < kIdxHeads; ++h) {
-      q.qf[h] = ld16(idx_q + ((size_t)t * kIdxHeads + h) * kIdxDim + d0);
-      q.w[h] = idx_w[(size_t)t * kIdxHeads + h];
-    }
+    for (int kc = 0; kc < 4; ++kc)
+      q.af[kc] = h < kIdxHeads
+                     ? ld16(idx_q + ((size_t)t * kIdxHeads + h) * kIdxDim + 32 * kc + 8 * (lane >> 4))
+                     : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < kIdxHeads; ++j) q.w[j] = idx_w[(size_t)t * kIdxHeads + j];
   };
+  // the group's 16 block scores on MFMA: lanes 0..15 receive the 4 head dots of block l
   auto compute = [&](int i, const u32x4_t (&kv)[4], const QueryRows& q) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float s = 0.f;
-#pragma unroll
-      for (int h = 0; h < kIdxHeads; ++h) {
-        float a = dot2(kv[r].x, q.qf[h].x, 0.f);
-        a = dot2(kv[r].y, q.qf[h].y, a);
-        a = dot2(kv[r].z, q.qf[h].z, a);
-        a = dot2(kv[r].w, q.qf[h].w, a);
-        a = row16_sum(a);
-        s += q.w[h] * fmaxf(a, 0.f);
-      }
-      if ((lane & 15) == 0) s_out[i * kScoreGroup + 4 * r + row_in_step] = s;
-    }
+    for (int kc = 0; kc < 4; ++kc) acc = mfma16(q.af[kc], kv[kc], acc);
+    const float s = head_mix(acc, q.w);
+    if (lane < kScoreGroup) s_out[i * kScoreGroup + lane] = s;
   };
 
   if (kIngest && (int)blockIdx.x < nq) {
@@ -192,12 +183,8 @@ __device__ __forceinline__ void score_body(
     m.g = (n_c - 1) / kScoreGroup;
     m.n_c = n_c;
     m.pt_row = page_table + (size_t)b * pt_stride;
-    int pg[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pg[r] = m.pt_row[block_of(m, r) / bpp];
-      QSA_CHECK(pg[r] >= 0);
-    }
+    const int pg = m.pt_row[block_of(m) / bpp];
+    QSA_CHECK(pg >= 0);
     QueryRows q;
     query_load(t, q);
     const int j = lane & 15;
@@ -207,10 +194,11 @@ __device__ __forceinline__ void score_body(
       key_block_mean(src, j, mean);
     }
     u32x4_t kv[4];
+    {   // the new block's row is stale here; it is replaced below
+      const int c = block_of(m);
+      const uint16_t* krow = ing->comp + ((int64_t)pg * bpp + (c % bpp)) * kIdxDim + 8 * (lane >> 4);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {   // the new block's row is stale here; it is replaced below
-      const int c = block_of(m, r);
-      kv[r] = ld16(ing->comp + ((int64_t)pg[r] * bpp + (c % bpp)) * kIdxDim + d0);
+      for (int kc = 0; kc < 4; ++kc) kv[kc] = ld16(krow + 32 * kc);
     }
     if (fresh) {
       __shared__ __attribute__((aligned(16))) u32x2_t s_key[kIdxDim / 4];
@@ -235,11 +223,11 @@ __device__ __forceinline__ void score_body(
         s_key[16 + j] = hi;     // dims 64+4j..64+4j+3
       }
       __syncthreads();
-      const u32x4_t nkey = *reinterpret_cast<const u32x4_t*>(
-          reinterpret_cast<const uint16_t*>(s_key) + d0);
+      if (block_of(m) == c) {
+        const uint16_t* nkey = reinterpret_cast<const uint16_t*>(s_key) + 8 * (lane >> 4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (block_of(m, r) == c) kv[r] = nkey;
+        for (int kc = 0; kc < 4; ++kc) kv[kc] = *reinterpret_cast<const u32x4_t*>(nkey + 32 * kc);
+      }
     }
     if (lane == 0) s_tg[0] = (t << 16) | m.g;
     compute(0, kv, q);
@@ -254,18 +242,18 @@ __device__ __forceinline__ void score_body(
 
     // pipeline: at step i the page entries of group i+2 and the keys of group i+1
     // are requested, then group i is scored
-    int pg0[4], pg1[4];
+    int pg0, pg1 = 0;
     u32x4_t kv0[4], kv1[4];
     QueryRows q0, q1;
     int t0 = meta(0).t;
     query_load(t0, q0);
-    pt_load(0, pg0);
-    if (ng > 1) pt_load(1, pg1);
+    pg0 = pt_load(0);
+    if (ng > 1) pg1 = pt_load(1);
     key_load(0, pg0, kv0);
     int tq1 = t0;
     for (int i = 0; i < ng; i += 2) {
       // even step: group i in kv0 / q0
-      if (i + 2 < ng) pt_load(i + 2, pg0);
+      if (i + 2 < ng) pg0 = pt_load(i + 2);
       if (i + 1 < ng) {
         tq1 = meta(i + 1).t;
         if (tq1 != t0) query_load(tq1, q1); else q1 = q0;
@@ -274,7 +262,7 @@ __device__ __forceinline__ void score_body(
       compute(i, kv0, q0);
       if (i + 1 >= ng) break;
       // odd step: group i+1 in kv1 / q1
-      if (i + 3 < ng) pt_load(i + 3, pg1);
+      if (i + 3 < ng) pg1 = pt_load(i + 3);
       if (i + 2 < ng) {
         t0 = meta(i + 2).t;
         if (t0 != tq1) query_load(t0, q0); else q0 = q1;
@@ -347,10 +335,6 @@ score_build_kernel(int nq, const uint16_t* __restrict__ idx_q, const float* __re
 // than a unit earlier.
 constexpr int kWin = 4;
 constexpr int kMultiWindows = 64;
-
-__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
-}
 
 struct Unit {
   int win, j, g;        // window (lane), leader query of the pass, group
