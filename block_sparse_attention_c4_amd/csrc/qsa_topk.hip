@@ -554,7 +554,8 @@ __device__ __forceinline__ void topk_row(int t, const float* __restrict__ scores
 //     is (about 650 per row), with the index of its first block.
 //   - The exact 512th largest key T and how many keys equal to T are kept come from
 //     radix passes of 8 bits over key - t0 by the whole group, one barrier each (the
-//     list's keys >= t0 lie between t0 and the row's largest maximum).
+//     list's keys >= t0 lie between t0 and the row's largest maximum); a pass whose
+//     chosen bin holds one key stops there and uses the bin as the threshold.
 //   - The kept blocks (keys above T) and the blocks whose key equals T are marked in
 //     two LDS bitmaps.  One block scan of the words' (greater, equal) counts gives
 //     each word the kept blocks before it, and each kept block is written to its slot
@@ -692,18 +693,34 @@ __device__ __forceinline__ uint2 units_lower_bound(const uint32_t (&uk)[U], int 
   return make_uint2(bin > 0 ? max(mn, float_key(fmn + (float)(bin - 1) / scale)) : mn, mx);
 }
 
+// The threshold of a select: a listed key k (nonzero, >= lo_key) is above it when
+// (k - lo_key) >> shift > q, equal to it when (k - lo_key) >> shift == q, and the
+// need_eq lowest-indexed keys equal to it are kept.
+struct Thresh {
+  uint32_t lo_key, q;
+  int shift, need_eq;
+};
+
+// 0 = below the threshold (or no key), 1 = equal, 2 = above.
+__device__ __forceinline__ int classify(uint32_t k, const Thresh& th) {
+  if (k == 0u) return 0;
+  const uint32_t d = (k - th.lo_key) >> th.shift;
+  return d > th.q ? 2 : (d == th.q ? 1 : 0);
+}
+
 // The kk-th largest of the keys held by the block (E per thread, 0 = none), all in
 // [lo_key, hi_key].  Radix passes of 8 bits over key - lo_key from the top of the
 // range, one barrier each: the histogram a pass fills was cleared during the
 // previous pass, and it clears the one the next pass fills (rhist[0] is cleared by
 // the caller before an earlier barrier).  A pass whose chosen bin holds a single key
-// ends the search with one more barrier.  Returns (T, how many keys equal to T are
-// kept); the same in every thread.
+// ends the search there: that key is the kk-th largest and the only one of its value,
+// so the threshold is its bin (no barrier to publish the key itself).  The same
+// Thresh in every thread.
 template <int E>
-__device__ __forceinline__ uint2 block_select(const uint32_t (&key)[E], uint32_t lo_key,
-                                              uint32_t hi_key, int kk) {
+__device__ __forceinline__ Thresh block_select(const uint32_t (&key)[E], uint32_t lo_key,
+                                               uint32_t hi_key, int kk) {
   const int tid = threadIdx.x;
-  if (hi_key <= lo_key) return make_uint2(hi_key, (uint32_t)kk);
+  if (hi_key <= lo_key) return Thresh{lo_key, 0u, 0, kk};   // every key equal
   int hi = 31 - __clz(hi_key - lo_key);
   uint32_t prefix = 0u;              // digits of key - lo_key found so far
   for (int pass = 0;; ++pass) {
@@ -721,15 +738,8 @@ __device__ __forceinline__ uint2 block_select(const uint32_t (&key)[E], uint32_t
     const int3 f = hist_find(H, kk);
     kk = f.y;
     prefix |= (uint32_t)f.x << lo;
-    if (lo == 0) return make_uint2(lo_key + prefix, (uint32_t)kk);   // every key of the bin is equal
-    if (f.z == 1) {                  // one key left: its holder publishes it
-      const uint32_t pm = ~((1u << lo) - 1u);
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (key[e] && ((key[e] - lo_key) & pm) == prefix) sf.misc[2] = (int)key[e];
-      __syncthreads();
-      return make_uint2((uint32_t)sf.misc[2], 1u);
-    }
+    if (lo == 0) return Thresh{lo_key, prefix, 0, kk};   // every key of the bin is equal
+    if (f.z == 1) return Thresh{lo_key, prefix >> lo, lo, 1};
     hi = lo - 1;
   }
 }
@@ -983,19 +993,18 @@ __device__ __forceinline__ void topk_row_fast(int t, const float* __restrict__ s
       lk[4 * e + j] = (i < n4 && k >= t_low) ? k : 0u;
     }
   }
-  const uint2 thr = block_select<kF4T * 4>(lk, t_low, row_max, kTopK);
-  const uint32_t T = thr.x;
-  const int need_eq = (int)thr.y;
+  const Thresh th = block_select<kF4T * 4>(lk, t_low, row_max, kTopK);
+  const int need_eq = th.need_eq;
 
   // ---- mark the blocks above T and those equal to T
 #pragma unroll
   for (int e = 0; e < kF4T; ++e)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t k = lk[4 * e + j];
-      if (k >= T) {                    // (a key of 0 is below every T)
+      const int cl = classify(lk[4 * e + j], th);
+      if (cl > 0) {
         const int cc = lc[e] + j;
-        atomicOr(k > T ? &sf.gtb[cc >> 5] : &sf.eqb[cc >> 5], 1u << (cc & 31));
+        atomicOr(cl == 2 ? &sf.gtb[cc >> 5] : &sf.eqb[cc >> 5], 1u << (cc & 31));
       }
     }
   __syncthreads();
@@ -1030,14 +1039,14 @@ __device__ __forceinline__ void topk_row_fast(int t, const float* __restrict__ s
   }
   __syncthreads();
   // ---- emit: each kept block goes from the thread that holds its key to slot (above
-  // before it) + min(equal before it, need_eq); a block equal to T is kept while fewer
-  // than need_eq equal blocks precede it
+  // before it) + min(equal before it, need_eq); a block equal to the threshold is kept
+  // while fewer than need_eq equal blocks precede it
 #pragma unroll
   for (int e = 0; e < kF4T; ++e)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t k = lk[4 * e + j];
-      if (k >= T) {
+      const int cl = classify(lk[4 * e + j], th);
+      if (cl > 0) {
         const int cc = lc[e] + j;
         const int w = cc >> 5;
         const uint32_t below = (1u << (cc & 31)) - 1u;
@@ -1045,7 +1054,7 @@ __device__ __forceinline__ void topk_row_fast(int t, const float* __restrict__ s
         const int g_below = (int)(pw & 0xffffu) + __popc(sf.gtb[w] & below);
         const int e_below = (int)(pw >> 16) + __popc(sf.eqb[w] & below);
         int out = -1;
-        if (k > T) out = g_below + min(e_below, need_eq);
+        if (cl == 2) out = g_below + min(e_below, need_eq);
         else if (e_below < need_eq) out = g_below + e_below;
         if (out >= 0 && out < kTopK) {   // exactly kTopK are kept; the guard bounds the row
           row_b[out] = cc;
