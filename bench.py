@@ -385,7 +385,8 @@ class OracleBaseline:
             if self.pool is None:
                 return dict(single, single_thread=dict(single))
             # every worker: the same units, cycled through the pool, for about `seconds`
-            self.pool.map(oracle_unit, tasks[:self.workers] * 1, chunksize=1)   # warm, untimed
+            warm = (tasks * (self.workers // len(tasks) + 1))[:self.workers]
+            self.pool.map(oracle_unit, warm, chunksize=1)   # maps the inputs, untimed
             done, t0 = 0, time.perf_counter()
             rounds = max(1, (4 * self.workers + len(tasks) - 1) // len(tasks))
             while time.perf_counter() - t0 < seconds:
