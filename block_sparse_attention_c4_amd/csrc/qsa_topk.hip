@@ -1009,8 +1009,10 @@ __device__ __forceinline__ void topk_row_fast(int t, const float* __restrict__ s
     }
   __syncthreads();
 
-  // ---- per bitmap word, the blocks above T and equal to T before it (thread i owns
-  // words kBWT i .. kBWT i + kBWT - 1)
+  // ---- per bitmap word, the blocks above T and equal to T before it within its wave
+  // (thread i owns words kBWT i .. kBWT i + kBWT - 1), and per wave its totals; the
+  // emit adds the totals of the waves before.  Counts are packed (equal << 16 | above):
+  // a set bit is a listed key, at most 4 kF4 of them, so neither half carries.
   {
     uint32_t gc[kBWT], ec[kBWT];
 #pragma unroll
@@ -1018,41 +1020,40 @@ __device__ __forceinline__ void topk_row_fast(int t, const float* __restrict__ s
       gc[i] = __popc(sf.gtb[kBWT * tid + i]);
       ec[i] = __popc(sf.eqb[kBWT * tid + i]);
     }
-    uint32_t gt = 0u, eq = 0u;
+    uint32_t v = 0u;
+#pragma unroll
+    for (int i = 0; i < kBWT; ++i) v += (ec[i] << 16) | gc[i];
+    const uint32_t inc = (uint32_t)wave_inclusive_sum((int)v);
+    if ((tid & 63) == 63) sf.wsum[tid >> 6] = inc;
+    uint32_t run = inc - v;
 #pragma unroll
     for (int i = 0; i < kBWT; ++i) {
-      gt += gc[i];
-      eq += ec[i];
+      sf.pre[kBWT * tid + i] = run;
+      run += (ec[i] << 16) | gc[i];
     }
-    // (a set bit is a listed key: at most 4 kF4 of them, so both counts fit 16 bits)
-    const uint2 sc = fscan((eq << 16) | gt);
-    uint32_t rg = sc.x & 0xffffu, re = sc.x >> 16;
-    uint32_t o[kBWT];
-#pragma unroll
-    for (int i = 0; i < kBWT; ++i) {
-      o[i] = (re << 16) | rg;
-      rg += gc[i];
-      re += ec[i];
-    }
-#pragma unroll
-    for (int i = 0; i < kBWT; ++i) sf.pre[kBWT * tid + i] = o[i];
   }
   __syncthreads();
   // ---- emit: each kept block goes from the thread that holds its key to slot (above
   // before it) + min(equal before it, need_eq); a block equal to the threshold is kept
   // while fewer than need_eq equal blocks precede it
 #pragma unroll
-  for (int e = 0; e < kF4T; ++e)
+  for (int e = 0; e < kF4T; ++e) {
+    // a float4's 4 blocks lie in one bitmap word (its first block is a multiple of 4);
+    // an entry past the list holds no key, and its word index is only kept in range
+    const int w = min(max(lc[e] >> 5, 0), kBWords - 1);
+    const int ow = (w / kBWT) >> 6;    // the wave of the word's owner
+    uint32_t pw = sf.pre[w];
+#pragma unroll
+    for (int i = 0; i < kFW; ++i) pw += i < ow ? sf.wsum[i] : 0u;
+    const uint32_t gw = sf.gtb[w], ew = sf.eqb[w];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int cl = classify(lk[4 * e + j], th);
       if (cl > 0) {
         const int cc = lc[e] + j;
-        const int w = cc >> 5;
         const uint32_t below = (1u << (cc & 31)) - 1u;
-        const uint32_t pw = sf.pre[w];
-        const int g_below = (int)(pw & 0xffffu) + __popc(sf.gtb[w] & below);
-        const int e_below = (int)(pw >> 16) + __popc(sf.eqb[w] & below);
+        const int g_below = (int)(pw & 0xffffu) + __popc(gw & below);
+        const int e_below = (int)(pw >> 16) + __popc(ew & below);
         int out = -1;
         if (cl == 2) out = g_below + min(e_below, need_eq);
         else if (e_below < need_eq) out = g_below + e_below;
@@ -1063,6 +1064,7 @@ __device__ __forceinline__ void topk_row_fast(int t, const float* __restrict__ s
         }
       }
     }
+  }
   const int base = kBlock * kTopK;
   for (int i = base + tid; i < sel_stride; i += kFT) {
     const int kq = i - base;
