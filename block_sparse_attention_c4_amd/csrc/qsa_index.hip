@@ -64,8 +64,9 @@ __device__ __forceinline__ int groups_of(int p) {
 // with the key taken from LDS.  The other work groups score every group but the
 // last of each query.  No work group reads memory that another one writes.
 constexpr int kWaveGroups = 64;
-// Waves of a decode scorer launch: 3 per SIMD, all resident at once (batch-32 decode
-// 17.8 us against 18.1 us with 4096 waves and 18.2 us with 2048).
+// Waves of a scorer launch (at most): 3 per SIMD, all resident at once (batch-32
+// decode 17.8 us against 18.1 us with 4096 waves and 18.2 us with 2048; the
+// multi-query scorer of batch-32 verification 22.1 against 22.6 us with 4096).
 constexpr int kScorerWaves = 3072;
 
 struct GroupMeta {
@@ -559,7 +560,7 @@ hipError_t launch_index(const IndexArgs& a, hipStream_t stream) {
       const int nq = std::min(kQPerLaunch, a.total_q - q0);
       // passes: one per window, plus one per request boundary inside a window
       const int64_t passes = std::min<int64_t>(nq, (nq + kWin - 1) / kWin + a.batch - 1);
-      const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(passes * gpq / 2, 4096));
+      const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(passes * gpq / 2, kScorerWaves));
       QSA_LAUNCH(score_multi_kernel, dim3(grid), dim3(64), 0, stream, nq,
                          a.idx_q + (size_t)q0 * kIdxHeads * kIdxDim,
                          a.idx_w + (size_t)q0 * kIdxHeads, a.q_req + q0, a.q_pos + q0,
