@@ -39,6 +39,8 @@
  *  - Raw K/V pool (the ordinary paged cache): k_pool, v_pool [slots, Hkv, D].
  *    Token t of request b lives in slot
  *        page_table[b * pt_stride + t / page_size] * page_size + t % page_size.
+ *    Page-table entries are >= 0 where a position is read, and slot indices
+ *    are below 2^31 (a pool of 2^31 slots would hold 2 TB of bf16 K).
  *  - Compressed key cache: comp_cache [slots / 4, idx_dim].  Block c (tokens
  *    4c..4c+3) of request b lives at row  slot(4c) / 4  (the block's first
  *    slot over 4, page aligned), so it follows the page's ownership.
