@@ -9,7 +9,13 @@ against the oracle: decode through the separate builder and indexer calls and
 through the folded call, prefill chunks through the MFMA scorer and through the
 multi-query scorer, target verification, and IndexShare reuse steps; decode and
 prefill also with FP8 K/V pools.
+
+An optional wide sweep (QSA_SHAPE_SWEEP=first:last, one case per seed) draws every
+page size from 16 to 256 tokens, contexts up to 262144 positions, batches up to 70
+requests and chunks up to 199 queries.
 """
+
+import os
 
 import numpy as np
 import pytest
@@ -20,6 +26,9 @@ from tests import test_gpu_parity as G
 pytestmark = pytest.mark.gpu
 
 PAGE_SIZES = (32, 48, 80, 128, 256)
+# the optional wide sweep also draws the pages the other cases use
+WIDE_PAGE_SIZES = (16, 32, 48, 64, 80, 128, 256)
+KINDS = ("decode", "prefill_mfma", "prefill_multi", "indexshare")
 
 
 def _lengths(rng, n, lo, hi):
@@ -30,28 +39,34 @@ def _lengths(rng, n, lo, hi):
     return np.maximum(x, lo)
 
 
-def _case(kind, seed):
-    """(workload, description) of the case's seed."""
+def _case(kind, seed, wide=False):
+    """The workload of the case's seed.  wide: contexts up to 262144 positions,
+    batches up to 70 requests, chunks up to 199 queries, every page size."""
     rng = np.random.default_rng(seed)
-    ps = int(rng.choice(PAGE_SIZES))
-    name = f"{kind}_s{seed}_p{ps}"
+    ps = int(rng.choice(WIDE_PAGE_SIZES if wide else PAGE_SIZES))
+    name = f"{'w' if wide else ''}{kind}_s{seed}_p{ps}"
     if kind == "decode":
-        B = int(rng.integers(1, 13))
-        return synth.make_workload(name, "decode", seed, _lengths(rng, B, 1, 40000),
-                                   hot_per_req=int(rng.integers(0, 5)), page_size=ps)
+        B = int(rng.choice((1, 3, 17, 40, 70))) if wide else int(rng.integers(1, 13))
+        return synth.make_workload(name, "decode", seed,
+                                   _lengths(rng, B, 1, 262144 if wide else 40000),
+                                   hot_per_req=int(rng.integers(0, 9 if wide else 5)), page_size=ps)
     if kind == "prefill_mfma":     # at least 64 queries and 16 per request
         B = int(rng.integers(1, 4))
-        chunk = int(rng.integers(max(16, (64 + B - 1) // B), 81))
-        return synth.make_workload(name, "prefill", seed, _lengths(rng, B, chunk, 40000),
-                                   chunk=chunk, hot_per_req=int(rng.integers(0, 5)), page_size=ps)
+        chunk = int(rng.integers(max(16, (64 + B - 1) // B), 200 if wide else 81))
+        return synth.make_workload(name, "prefill", seed,
+                                   _lengths(rng, B, chunk, 140000 if wide else 40000),
+                                   chunk=chunk, hot_per_req=int(rng.integers(0, 9 if wide else 5)),
+                                   page_size=ps)
     if kind == "prefill_multi":    # 2..8 queries per request
-        B = int(rng.integers(2, 13))
+        B = int(rng.integers(2, 40 if wide else 13))
         chunk = int(rng.integers(2, 9))
-        return synth.make_workload(name, "prefill", seed, _lengths(rng, B, chunk, 40000),
+        return synth.make_workload(name, "prefill", seed,
+                                   _lengths(rng, B, chunk, 140000 if wide else 40000),
                                    chunk=chunk, page_size=ps)
     if kind == "indexshare":
-        B = int(rng.integers(1, 5))
-        return synth.make_workload(name, "indexshare", seed, _lengths(rng, B, 1, 40000),
+        B = int(rng.integers(1, 6 if wide else 5))
+        return synth.make_workload(name, "indexshare", seed,
+                                   _lengths(rng, B, 1, 262140 if wide else 40000),
                                    reuse_steps=3, page_size=ps)
     raise ValueError(kind)
 
@@ -87,3 +102,36 @@ def test_random_shape_end_to_end_fp8(kind, seed):
     wl = synth.with_fp8_kv(_case(kind, seed))
     _log(wl)
     G._check_e2e(wl, kv="fp8")
+
+
+def _sweep_seeds():
+    """Seeds of the optional wide sweep, QSA_SHAPE_SWEEP="first:last" (unset: none)."""
+    spec = os.environ.get("QSA_SHAPE_SWEEP", "")
+    if not spec:
+        return []
+    first, last = (int(x) for x in spec.split(":"))
+    return list(range(first, last))
+
+
+@pytest.mark.skipif(not _sweep_seeds(), reason="the wide sweep runs with QSA_SHAPE_SWEEP=first:last")
+@pytest.mark.parametrize("seed", _sweep_seeds() or [0])
+def test_random_shape_sweep(seed):
+    """Wide shapes: the path is seed % 4 of KINDS; every fifth seed of the decode and
+    MFMA-prefill paths uses FP8 pools.  Prefill chunks through the MFMA scorer check
+    the attention of 64 sampled rows (the selection of every row)."""
+    kind = KINDS[seed % 4]
+    fp8 = seed % 5 == 0 and kind in ("decode", "prefill_mfma")
+    wl = _case(kind, seed, wide=True)
+    if fp8:
+        wl = synth.with_fp8_kv(wl)
+    _log(wl)
+    try:
+        if kind == "indexshare":
+            G._check_indexshare(wl)
+        else:
+            G._check_e2e(wl, sample=64 if kind == "prefill_mfma" else None, kv="fp8" if fp8 else "bf16")
+            if kind == "decode" and not fp8:
+                G._check_fused_equals_separate(wl)
+    finally:
+        G._CACHE.clear()
+
