@@ -8,7 +8,8 @@ all from the case's seed.  Each path runs end to end and is checked on every row
 against the oracle: decode through the separate builder and indexer calls and
 through the folded call, prefill chunks through the MFMA scorer and through the
 multi-query scorer, target verification, and IndexShare reuse steps; decode and
-prefill also with FP8 K/V pools.
+prefill also with FP8 K/V pools, and with 3-D MRoPE positions (random vision spans,
+random maps of rotary pairs to axes).
 
 An optional wide sweep (QSA_SHAPE_SWEEP=first:last, one case per seed) draws every
 page size from 16 to 256 tokens, contexts up to 262144 positions, batches up to 70
@@ -102,6 +103,44 @@ def test_random_shape_end_to_end_fp8(kind, seed):
     wl = synth.with_fp8_kv(_case(kind, seed))
     _log(wl)
     G._check_e2e(wl, kv="fp8")
+
+
+def _spans(rng, L):
+    """0-3 sorted, non-overlapping vision spans (start, T, H, W) in a stream of L tokens
+    (a span may run past the end, which cuts it)."""
+    out, t = [], 0
+    for _ in range(int(rng.integers(0, 4))):
+        if t >= L:
+            break
+        T, H, W = int(rng.integers(1, 4)), int(rng.integers(1, 33)), int(rng.integers(1, 33))
+        start = int(rng.integers(t, L))
+        out.append((start, T, H, W))
+        t = start + T * H * W
+    return out
+
+
+def _mrope_case(kind, seed):
+    """A case of _case with 3-D positions: random vision spans per request and a
+    contiguous, interleaved or random map of rotary pairs to axes."""
+    wl = _case(kind, seed)
+    rng = np.random.default_rng(seed + 7919)
+    pick = int(rng.integers(3))
+    axis = None if pick == 0 else (np.arange(64) % 3 if pick == 1 else rng.integers(0, 3, size=64))
+    return synth.with_mrope(wl, [_spans(rng, int(L)) for L in wl.lengths], pair_axis=axis)
+
+
+MROPE_CASES = ([("decode", s) for s in (461, 462, 463)]
+               + [("prefill_mfma", s) for s in (471, 472)] + [("prefill_multi", s) for s in (481, 482)])
+
+
+@pytest.mark.parametrize("kind,seed", MROPE_CASES)
+def test_random_shape_end_to_end_mrope(kind, seed):
+    wl = _mrope_case(kind, seed)
+    _log(wl)
+    G._check_e2e(wl)
+    if kind == "decode":
+        G._check_fused_equals_separate(wl)
+        G._check_e2e_fused(wl)
 
 
 def _sweep_seeds():
