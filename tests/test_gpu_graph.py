@@ -119,3 +119,21 @@ def test_graph_indexshare_reuse_step():
     dw.step()
     dw.set_reuse(2)
     _replays_match(dw, lambda: dw.reuse_step(2), [dw.out, dw.lse], fill=[dw.out, dw.lse])
+
+
+def test_graph_decode_step_noalloc():
+    # the allocation-free attention call, made for callers under capture: the folded
+    # index call and qsa_sparse_gqa_decode_noalloc captured together (its scratch
+    # address is taken by the eager step that precedes the capture)
+    from block_sparse_attention_c4_amd import binding as B
+    wl = synth.make_workload("g_decode_na", "decode", 335, [4, 2052, 9003, 40000, 700, 131072],
+                             hot_per_req=2)
+    dw = _device(wl)
+    assert dw.can_fuse()
+
+    def step():
+        dw.build_index()
+        B.qsa_sparse_gqa_decode_noalloc(dw.dims, dw.batch, dw.q, dw.k_pool, dw.v_pool, dw.page_table,
+                                        dw.pt_stride, dw.sel_pos, dw.sel_count, runner.SEL_STRIDE,
+                                        None, 0, dw.out, dw.lse)
+    _replays_match(dw, step, _outputs(dw))
