@@ -403,7 +403,7 @@ class OracleBaseline:
 # ------------------------------------------------------------------ GPU timing
 
 def capture_round(torch, fns, outs, refs):
-    """One hipGraph that runs every callable once, in order (one step per input copy).
+    """One hipGraph that runs every callable once, in order (steps cycling the input copies).
     refs[i] is the eager result of fns[i] (in outs[i]); the graph is replayed twice and
     every output is checked against its eager result.  A replay covers len(fns) steps,
     so the fixed cost of launching a graph (about 4.5 us here) is paid once per round."""
@@ -746,8 +746,13 @@ def measure(args, name, steps, warmup, nsets, K):
     ref_out = base.out.clone()
 
     def timed(fns, outs, refs):
-        """ms per call of fns (cycled), as replays of one hipGraph per round of
-        len(fns) calls unless --no-graph."""
+        """ms per call of fns (cycled), as replays of one hipGraph unless --no-graph.
+        A replay runs the calls in order, repeated so that it holds up to 16 calls
+        when the timed steps fill at least 8 replays: the fixed cost of launching a
+        graph (about 4.5 us here) is then shared by up to 16 steps, as it is when a
+        step is part of a larger captured forward pass."""
+        rounds = max(1, min(16 // len(fns), steps // (8 * len(fns))))
+        fns, outs, refs = fns * rounds, outs * rounds, refs * rounds
         graph = None
         if not args.no_graph:
             try:
